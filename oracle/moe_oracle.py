@@ -1,0 +1,269 @@
+"""Float64 CPU oracle of the MoE experts path (test infrastructure only).
+
+Sources (the vLLM API pages this follows):
+  * "vllm.model_executor.layers.fused_moe.experts.moonep_experts", module
+    docstring: with rows contiguous per weight row, the experts step is a
+    grouped GEMM for the gate projection and one for the up projection, the
+    SiLU-gated product scaled per row by its route weight, and a grouped GEMM
+    for the down projection; segments with no rows are skipped.
+  * same page, MoonEPExperts.apply: cu_seqlens = cumsum of per-row token
+    counts (int32 end offsets, one per weight row); route weights applied to
+    the activation before the down GEMM; rows past the last end are zero.
+  * same page, moonep_grouped_gemm: each segment's rows are multiplied by the
+    transpose of that segment's [N, K] weight (weights stored [G, N, K]).
+  * "vllm.model_executor.layers.fused_moe.experts.flashinfer_moe_ep", module
+    docstring and FlashInferMoeEpExperts.apply: route on the top-k output, then
+    compute and combine back to token order (the finalize is a no-op because
+    the kernel already reduced); ids are int32.
+  * "vllm.model_executor.layers.fused_moe.experts.trtllm_mxfp4_moe",
+    TrtLlmMxfp4ExpertsBase: MXFP4 weights (kMxfp4Static with unquantized
+    activations) and the SwiGLU-OAI activation parameterised by alpha, beta
+    and a clamp limit; the SiTu closed form in the constructor's comment.
+
+Readings where the pages are silent:
+  * SwiGLU-OAI: g' = min(g, limit), u' = clamp(u, -limit, limit),
+    f = g' * sigmoid(alpha * g') * (u' + beta)  (the gpt-oss definition).
+  * MXFP4 = OCP Microscaling v1.0: e2m1 codes (sign, 2-bit exponent with bias
+    1, 1-bit mantissa), two per byte, element 2i in the low nibble; one e8m0
+    scale byte per 32 consecutive K elements, value 2^(v-127), v=255 is NaN.
+  * Order inside a segment: ascending flat slot index t*k + j.
+  * Expert id -1 marks a masked slot (contributes nothing, no error); any other
+    id outside [0, E) is skipped and counted as bad.
+  * Combine sums the k slot results of a token in ascending j.
+
+Everything is computed in float64 from exactly widened inputs.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Optional, Sequence, Tuple, Union
+
+import numpy as np
+
+__all__ = [
+    "align", "grouped_mm", "silu", "swiglu_oai", "situ", "activation",
+    "mxfp4_decode", "expert_matrix", "experts_grouped", "experts_forward",
+    "experts_forward_literal", "pregrouped_forward",
+]
+
+# A weight argument is either a float array [E, N, K] or, for MXFP4, a pair
+# (codes uint8 [E, N, K/2], scales uint8 [E, N, K/32]).
+Weight = Union[np.ndarray, Tuple[np.ndarray, np.ndarray]]
+
+
+# ----------------------------------------------------------------------------
+# Grouping: histogram, prefix sum, stable permutation.
+# moonep_experts page, MoonEPExperts.apply (cu_seqlens as a cumulative sum of
+# per-row counts) and module docstring (rows contiguous per weight row).
+# ----------------------------------------------------------------------------
+def align(topk_ids: np.ndarray, E: int):
+    """Group the T*k routed slots by expert.
+
+    Returns a dict with
+      counts   int64 [E]   slots routed to each expert (valid ids only)
+      cu_seqlens int64 [E] cumulative end offsets (cumsum of counts)
+      offsets  int64 [E+1] segment starts, offsets[E] = number of valid slots
+      perm     int64 [M]   perm[p] = flat slot index i = t*k + j at sorted row p,
+                           ascending in i inside each segment
+      inv_perm int64 [T*k] inv_perm[i] = p, or -1 for masked / bad slots
+      n_bad    int         ids outside [0, E) other than -1
+    """
+    flat = np.asarray(topk_ids).reshape(-1).astype(np.int64)
+    valid = (flat >= 0) & (flat < E)
+    n_bad = int(np.sum((flat != -1) & ~valid))
+    counts = np.bincount(flat[valid], minlength=E).astype(np.int64)
+    cu = np.cumsum(counts)
+    offsets = np.concatenate([[0], cu]).astype(np.int64)
+    # stable sort by expert; masked and bad slots get key E and fall off the end
+    key = np.where(valid, flat, E)
+    order = np.argsort(key, kind="stable")
+    M = int(offsets[E])
+    perm = order[:M].astype(np.int64)
+    inv_perm = np.full(flat.size, -1, dtype=np.int64)
+    inv_perm[perm] = np.arange(M, dtype=np.int64)
+    return dict(counts=counts, cu_seqlens=cu, offsets=offsets, perm=perm,
+                inv_perm=inv_perm, n_bad=n_bad)
+
+
+# ----------------------------------------------------------------------------
+# Grouped GEMM. moonep_experts page, moonep_grouped_gemm.
+# ----------------------------------------------------------------------------
+def grouped_mm(a: np.ndarray, w_of: Callable[[int], np.ndarray], cu_seqlens: Sequence[int]) -> np.ndarray:
+    """Segment g's rows of `a` times the transpose of segment g's weight, for
+    segments given by end offsets.
+
+    `w_of(g)` returns segment g's [N, K] weight in float64. Rows past the last
+    end offset are zero; empty segments never ask for their weight."""
+    a = np.asarray(a, dtype=np.float64)
+    out = None
+    start = 0
+    for g, end in enumerate(cu_seqlens):
+        end = int(end)
+        if end > start:
+            wg = w_of(g)
+            if out is None:
+                out = np.zeros((a.shape[0], wg.shape[0]), dtype=np.float64)
+            out[start:end] = a[start:end] @ wg.T
+        start = end
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Activations.
+# ----------------------------------------------------------------------------
+def silu(g):
+    """silu(g) = g * sigmoid(g) (moonep_experts page, module docstring)."""
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu_oai(g, u, alpha: float, beta: float, limit: float):
+    """Clamped SwiGLU-OAI with the gemm1_alpha / gemm1_beta / clamp-limit
+    parameters named on the trtllm_mxfp4_moe page (TrtLlmMxfp4ExpertsBase).
+    The page gives no formula; this is the gpt-oss reading: the gate is capped
+    at `limit` from above, the up projection clamped to [-limit, limit], and
+    f = g' * sigmoid(alpha * g') * (u' + beta)."""
+    g = np.minimum(np.asarray(g, dtype=np.float64), limit)
+    u = np.clip(np.asarray(u, dtype=np.float64), -limit, limit)
+    return g / (1.0 + np.exp(-alpha * g)) * (u + beta)
+
+
+def situ(g, u, alpha: float, beta: float):
+    """SiTu gated activation (trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsBase
+    constructor comment): left = alpha*tanh(g/alpha)*sigmoid(g) on the gate,
+    right = beta*tanh(u/beta) on the up projection, product of the two."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    return alpha * np.tanh(g / alpha) / (1.0 + np.exp(-g)) * (beta * np.tanh(u / beta))
+
+
+def activation(name: str, g, u, alpha=1.0, beta=0.0, limit=math.inf):
+    if name == "silu":
+        return silu(g) * np.asarray(u, dtype=np.float64)
+    if name == "swiglu_oai":
+        return swiglu_oai(g, u, alpha, beta, limit)
+    if name == "situ":
+        return situ(g, u, alpha, beta)
+    raise ValueError(f"unknown activation {name!r}")
+
+
+# ----------------------------------------------------------------------------
+# MXFP4 decoding (OCP Microscaling v1.0 reading; the pages only name the format).
+# ----------------------------------------------------------------------------
+def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Exact float64 value of MXFP4 weights.
+
+    codes [..., K/2] uint8: element 2i in the low nibble of byte i, 2i+1 high.
+    Each e2m1 code is s|e1 e0|m: for e > 0 the value is (-1)^s 2^(e-1) (1+m/2),
+    for e = 0 it is (-1)^s m/2. scales [..., K/32] uint8: one e8m0 byte per 32
+    consecutive elements, value 2^(v-127), and v = 255 is NaN."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    lo = codes & 0x0F
+    hi = codes >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2).astype(np.int64)
+    sign = np.where(nib & 0x8, -1.0, 1.0)
+    e = (nib >> 1) & 0x3
+    m = (nib & 0x1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, (e - 1).astype(np.int32)))
+    val = sign * mag
+    s = np.asarray(scales, dtype=np.uint8).astype(np.int64)
+    sc = np.where(s == 255, np.nan, np.ldexp(1.0, (s - 127).astype(np.int32)))
+    sc = np.repeat(sc, 32, axis=-1)
+    return val * sc
+
+
+def expert_matrix(w: Weight, e: int) -> np.ndarray:
+    """Expert e's [N, K] weight in float64 (decoded when MXFP4)."""
+    if isinstance(w, tuple):
+        codes, scales = w
+        return mxfp4_decode(codes[e], scales[e])
+    return np.asarray(w[e], dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# The experts computation in grouped form.
+# moonep_experts page, module docstring + MoonEPExperts.apply.
+# ----------------------------------------------------------------------------
+def experts_grouped(x_rows: np.ndarray, cu_seqlens: Sequence[int], route_w: np.ndarray,
+                    w_gate: Weight, w_up: Weight, w_down: Weight,
+                    act: str = "silu", alpha=1.0, beta=0.0, limit=math.inf) -> np.ndarray:
+    """Rows already contiguous per weight row: gate and up grouped GEMMs, the
+    activation times the per-row route weight, the down grouped GEMM. Rows past
+    the last end offset come out zero."""
+    x_rows = np.asarray(x_rows, dtype=np.float64)
+    NvS = x_rows.shape[0]
+    H = x_rows.shape[1]
+    gate = grouped_mm(x_rows, lambda g: expert_matrix(w_gate, g), cu_seqlens)
+    if gate is None:                                    # every segment empty
+        return np.zeros((NvS, H), dtype=np.float64)
+    up = grouped_mm(x_rows, lambda g: expert_matrix(w_up, g), cu_seqlens)
+    a = activation(act, gate, up, alpha, beta, limit)
+    a = a * np.asarray(route_w, dtype=np.float64)[:, None]
+    out = grouped_mm(a, lambda g: expert_matrix(w_down, g), cu_seqlens)
+    end = int(cu_seqlens[-1]) if len(cu_seqlens) else 0
+    out[end:] = 0.0
+    return out
+
+
+def experts_forward(x: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
+                    w_gate: Weight, w_up: Weight, w_down: Weight,
+                    act: str = "silu", alpha=1.0, beta=0.0, limit=math.inf) -> np.ndarray:
+    """Token-major MoE experts layer: group the routed slots by expert, run
+    the grouped computation, then combine each token's k slot results in
+    ascending j (flashinfer_moe_ep page: route, compute, combine)."""
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(topk_ids)
+    T, k = ids.shape
+    E = _num_experts(w_gate)
+    al = align(ids, E)
+    perm, inv = al["perm"], al["inv_perm"]
+    x_rows = x[perm // k]
+    rw = np.asarray(topk_weights, dtype=np.float64).reshape(-1)[perm]
+    y = experts_grouped(x_rows, al["cu_seqlens"], rw, w_gate, w_up, w_down, act, alpha, beta, limit)
+    out = np.zeros((T, x.shape[1]), dtype=np.float64)
+    for t in range(T):
+        acc = np.zeros(x.shape[1], dtype=np.float64)
+        for j in range(k):
+            p = inv[t * k + j]
+            if p >= 0:
+                acc = acc + y[p]
+        out[t] = acc
+    return out
+
+
+def experts_forward_literal(x, topk_ids, topk_weights, w_gate, w_up, w_down,
+                            act="silu", alpha=1.0, beta=0.0, limit=math.inf) -> np.ndarray:
+    """The per-token definition: for each token and each of its k slots, run
+    the selected expert's MLP on the token, scale by the route weight, and sum
+    over the slots in ascending j. Masked (-1) and out-of-range ids add
+    nothing. Slow; for small problems and as a check of `experts_forward`."""
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(topk_ids)
+    wts = np.asarray(topk_weights, dtype=np.float64)
+    T, k = ids.shape
+    E = _num_experts(w_gate)
+    out = np.zeros((T, x.shape[1]), dtype=np.float64)
+    for t in range(T):
+        acc = np.zeros(x.shape[1], dtype=np.float64)
+        for j in range(k):
+            e = int(ids[t, j])
+            if e < 0 or e >= E:
+                continue
+            g = expert_matrix(w_gate, e) @ x[t]
+            u = expert_matrix(w_up, e) @ x[t]
+            a = activation(act, g, u, alpha, beta, limit) * wts[t, j]
+            acc = acc + expert_matrix(w_down, e) @ a
+        out[t] = acc
+    return out
+
+
+def pregrouped_forward(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down,
+                       act="silu", alpha=1.0, beta=0.0, limit=math.inf) -> np.ndarray:
+    """The pre-grouped entry: rows given in segment order with end offsets and
+    per-row route weights (moonep_experts page, MoonEPExperts.apply). Same as
+    `experts_grouped`; named for the entry point it checks."""
+    return experts_grouped(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, act, alpha, beta, limit)
+
+
+def _num_experts(w: Weight) -> int:
+    return (w[0] if isinstance(w, tuple) else w).shape[0]

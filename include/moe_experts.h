@@ -1,0 +1,204 @@
+/*
+ * moe_experts.h — C ABI of the MI355X (gfx950) MoE experts library.
+ *
+ * The library runs the experts step of a mixture-of-experts layer on one GPU:
+ * group the router's top-k slots by expert (histogram, prefix sum to segment
+ * end offsets, stable permutation), a grouped GEMM for the gate and up
+ * projections with the activation and route weight applied in its epilogue,
+ * a grouped GEMM for the down projection, and a fixed-order combine back to
+ * token order.
+ *
+ * Sources (vLLM API pages):
+ *   - "vllm.model_executor.layers.fused_moe.experts.moonep_experts": module
+ *     docstring (the three grouped GEMMs, route weight on the activation,
+ *     empty segments skipped), MoonEPExperts.apply (cu_seqlens as int32
+ *     cumulative end offsets, one per weight row; rows past the last end
+ *     zero-filled), moonep_grouped_gemm ([G, N, K] weights, K contiguous).
+ *   - "vllm.model_executor.layers.fused_moe.experts.flashinfer_moe_ep":
+ *     module docstring (route on the top-k output, compute and combine in the
+ *     experts step), FlashInferMoeEpExperts.apply (int32 ids, output written
+ *     in place, not accumulated).
+ *   - "vllm.model_executor.layers.fused_moe.experts.trtllm_mxfp4_moe":
+ *     TrtLlmMxfp4ExpertsBase (MXFP4 weights with bf16 activations, SwiGLU-OAI
+ *     with alpha / beta / clamp limit), workspace_shapes (output keeps the
+ *     unpadded hidden size).
+ *   - "vllm.models.deepseek_v4.nvidia.fi_moe": DeepseekV4MegaMoEExpertsFI
+ *     (workspace allocated before the first forward so warm-up and capture
+ *     never allocate; token capacity checked against a fixed maximum).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (device) are HIP device pointers; (host) are host.
+ *   - bf16 tensors are raw 16-bit bfloat16 words, row-major, last dim contiguous.
+ *   - Weights use the [E, N, K] layout: w_gate, w_up [E, I, H]; w_down [E, H, I].
+ *     MXFP4 weights are packed e2m1 codes [E, N, K/2] (element 2i in the low
+ *     nibble of byte i) with e8m0 scale bytes [E, N, K/32], one per 32
+ *     consecutive K elements (OCP Microscaling v1.0).
+ *   - The caller owns every buffer, including the workspace. The library never
+ *     allocates, frees or synchronises inside a forward call: it only enqueues
+ *     kernels on `stream` (a hipStream_t; NULL = the default stream).
+ *   - Inputs are read-only; outputs are overwritten.
+ *   - Calls with distinct workspaces may run concurrently. Two calls in flight
+ *     on one workspace race.
+ *   - Return 0 on success or a negative moe_status. Host-side validation is
+ *     O(1) and reads no device memory; a failing call enqueues nothing.
+ *     Problems found on the device (bad expert ids, malformed cu_seqlens) are
+ *     written to a status word in the workspace: read it with
+ *     moe_device_error() after the stream has been synchronised.
+ */
+#ifndef MOE_EXPERTS_H
+#define MOE_EXPERTS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* a hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,  /* null pointer, non-positive size, k > E, unknown enum, non-finite parameter */
+  MOE_ENOTSUP = -2, /* valid but unsupported: H or I not a multiple of 64, E > 4096, limit <= 0, ... */
+  MOE_ENOSPC = -3,  /* workspace smaller than the *_workspace_bytes() figure for this problem */
+  MOE_EHIP = -4     /* a HIP launch or query failed */
+} moe_status;
+
+/* Weight format. trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsBase._supports_quant_scheme
+ * (MXFP4 weights with unquantized activations); moonep_experts page (bf16). */
+typedef enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1 } moe_wfmt;
+
+/* Activation. moonep_experts page, module docstring (silu(gate) * up);
+ * trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsBase (SwiGLU-OAI with alpha, beta,
+ * clamp limit). SwiGLU-OAI is read as
+ *   g' = min(g, limit), u' = clamp(u, -limit, limit), f = g' * sigmoid(alpha g') * (u' + beta). */
+typedef enum { MOE_ACT_SILU = 0, MOE_ACT_SWIGLU_OAI = 1 } moe_act;
+
+typedef struct {
+  int32_t T;     /* tokens: rows of x and out (NvS for the pre-grouped entry) */
+  int32_t H;     /* hidden size (K of GEMM1, N of GEMM2); multiple of 64 */
+  int32_t I;     /* intermediate size (N of GEMM1, K of GEMM2); multiple of 64 */
+  int32_t E;     /* experts, i.e. weight rows (segments incl. redundant slots for the pre-grouped entry) */
+  int32_t k;     /* slots per token (ignored by the pre-grouped entry) */
+  int32_t wfmt;  /* moe_wfmt */
+  int32_t act;   /* moe_act */
+  float alpha;   /* SwiGLU-OAI only */
+  float beta;    /* SwiGLU-OAI only */
+  float limit;   /* SwiGLU-OAI only; > 0, may be +inf */
+} moe_problem;
+
+/* Byte offsets of the intermediates inside a forward workspace (for tests and
+ * tools; the forward call does not need them). Fields not used by a path are 0. */
+typedef struct {
+  size_t status;     /* int32[4]: [0] bad expert ids / malformed offsets, [1] valid slots M */
+  size_t counts;     /* int32[E]   rows per segment */
+  size_t cu_seqlens; /* int32[E]   cumulative end offsets */
+  size_t perm;       /* int32[T*k] sorted row -> flat slot t*k+j (first M entries) */
+  size_t inv_perm;   /* int32[T*k] flat slot -> sorted row, -1 for masked / bad ids */
+  size_t w_sorted;   /* float[T*k] route weight per sorted row */
+  size_t act;        /* bf16 [T*k, I] activation rows in sorted order */
+  size_t y;          /* bf16 [T*k, H] down-projection rows in sorted order */
+  size_t total;      /* = moe_experts_workspace_bytes() */
+} moe_ws_layout;
+
+/* Workspace bytes a moe_experts_forward call on problem *p needs (0 if *p is
+ * invalid). Depends only on the sizes in *p, so a workspace sized once for the
+ * largest T serves every smaller T (fi_moe page: allocate before the first
+ * forward). */
+size_t moe_experts_workspace_bytes(const moe_problem* p);
+
+/* Fills *layout for problem *p; MOE_EINVAL for an invalid problem. */
+int moe_experts_workspace_layout(const moe_problem* p, moe_ws_layout* layout);
+
+/*
+ * The experts step, token-major in and out.
+ *   x            (device) bf16 [T, H]
+ *   topk_ids     (device) int32 [T, k]; -1 = masked slot (contributes nothing);
+ *                any other id outside [0, E) is skipped and counted in the
+ *                workspace status word (moe_device_error)
+ *   topk_weights (device) float32 [T, k], applied to the activation before the
+ *                down projection
+ *   w_gate, w_up (device) [E, I, H] bf16, or MXFP4 codes [E, I, H/2]
+ *   w_down       (device) [E, H, I] bf16, or MXFP4 codes [E, H, I/2]
+ *   s_gate, s_up, s_down (device) e8m0 scales [E, N, K/32] for MXFP4, NULL for bf16
+ *   out          (device) bf16 [T, H], overwritten:
+ *                out[t] = sum over j = 0..k-1, in that order, in fp32, of
+ *                W_down[e] (f(W_gate[e] x[t], W_up[e] x[t]) * w[t,j]),  e = ids[t,j]
+ *   workspace    (device) at least moe_experts_workspace_bytes(p) bytes,
+ *                256-byte aligned
+ * Numerics: bf16 MFMA products with fp32 accumulation; the activation is
+ * rounded once to bf16 before the down GEMM and each slot's down-projection
+ * row once to bf16 before the fp32 combine.
+ */
+int moe_experts_forward(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                        const float* topk_weights, const void* w_gate, const void* w_up,
+                        const void* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                        const uint8_t* s_down, void* out, void* workspace, size_t workspace_bytes,
+                        moe_stream_t stream);
+
+/* Same as moe_experts_forward, and additionally records the caller's
+ * hipEvent_t handles stage_events[0..n_events-1] on `stream` between the
+ * stages (align, GEMM1, GEMM2, combine: event i before stage i, the last
+ * after the last stage) so a benchmark can time each kernel on the stream it
+ * runs on. n_events must be 0 (no recording) or 5. */
+int moe_experts_forward_timed(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                              const float* topk_weights, const void* w_gate, const void* w_up,
+                              const void* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                              const uint8_t* s_down, void* out, void* workspace,
+                              size_t workspace_bytes, moe_stream_t stream,
+                              void* const* stage_events, int n_events);
+
+/* Workspace bytes for moe_align on (T, k, E); 0 if invalid. */
+size_t moe_align_workspace_bytes(int32_t T, int32_t k, int32_t E);
+
+/*
+ * Grouping only (the forward's first stage, exposed for bit-exact testing).
+ * moonep_experts page, MoonEPExperts.apply (cumulative sum of per-row counts)
+ * and module docstring (rows contiguous per weight row).
+ *   topk_ids   (device) int32 [T, k]
+ *   counts     (device) int32 [E]     slots per expert (valid ids only)
+ *   cu_seqlens (device) int32 [E]     cumulative end offsets
+ *   perm       (device) int32 [T*k]   perm[p] = t*k+j for sorted row p, ascending
+ *                                     inside each segment; entries >= M are -1
+ *   inv_perm   (device) int32 [T*k]   inverse, -1 for masked / bad slots
+ *   workspace  (device) moe_align_workspace_bytes(T, k, E) bytes
+ */
+int moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
+              int32_t* cu_seqlens, int32_t* perm, int32_t* inv_perm, void* workspace,
+              size_t workspace_bytes, moe_stream_t stream);
+
+/* Workspace bytes for moe_experts_forward_grouped on *p (p->T = NvS,
+ * p->E = segments); 0 if invalid. */
+size_t moe_experts_grouped_workspace_bytes(const moe_problem* p);
+
+/*
+ * Pre-grouped experts step (moonep_experts page: rows already contiguous per
+ * weight row in segment order, [E+B] segments including redundant slots).
+ *   x_nvs      (device) bf16 [NvS, H], NvS = p->T
+ *   cu_seqlens (device) int32 [G] cumulative end offsets, G = p->E; must be
+ *              non-decreasing and <= NvS, else the status word is set and
+ *              the whole output is zero
+ *   route_w    (device) float32 [NvS]
+ *   weights / scales as in moe_experts_forward with E = G
+ *   out_nvs    (device) bf16 [NvS, H], overwritten; rows >= cu_seqlens[G-1] are 0
+ */
+int moe_experts_forward_grouped(const moe_problem* p, const void* x_nvs, const int32_t* cu_seqlens,
+                                const float* route_w, const void* w_gate, const void* w_up,
+                                const void* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                                const uint8_t* s_down, void* out_nvs, void* workspace,
+                                size_t workspace_bytes, moe_stream_t stream);
+
+/* Reads the device status word of a workspace used by moe_experts_forward,
+ * moe_experts_forward_grouped or moe_align: *n_bad = number of expert ids
+ * outside [0, E) other than -1 in the last call (or 1 if its cu_seqlens were
+ * malformed). Synchronous copy: call after the stream has finished. */
+int moe_device_error(const void* workspace, int32_t* n_bad);
+
+/* Static description of a status code. */
+const char* moe_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_EXPERTS_H */

@@ -1,0 +1,50 @@
+// Back to token order.
+//
+// flashinfer_moe_ep page, module docstring and FlashInferMoeEpExperts
+// (finalize_weight_and_reduce_impl is a no-op): the experts step itself
+// reduces each token's k slot results, and the output is written, not
+// accumulated. Here the sum runs over j = 0..k-1 in that order, in fp32, so
+// the result does not depend on scheduling (no atomics).
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+// One workgroup per token; each thread sums 8 consecutive columns.
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* y, const int32_t* inv_perm, int T, int k,
+                                                 int H, uint16_t* out) {
+  const int t = blockIdx.x;
+  if (t >= T) return;
+  for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int p = inv_perm[(size_t)t * k + j];
+      if (p < 0) continue;
+      const u32x4 v = *(const u32x4*)(y + (size_t)p * H + h);
+      const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += bf16_bits_to_f32(w[i] & 0xffffu);
+        acc[2 * i + 1] += bf16_bits_to_f32(w[i] >> 16);
+      }
+    }
+    u32x4 o;
+    o[0] = pack_bf16x2(acc[0], acc[1]);
+    o[1] = pack_bf16x2(acc[2], acc[3]);
+    o[2] = pack_bf16x2(acc[4], acc[5]);
+    o[3] = pack_bf16x2(acc[6], acc[7]);
+    *(u32x4*)(out + (size_t)t * H + h) = o;
+  }
+}
+
+// Pre-grouped entry: zero rows [status[1], NvS) of out (moonep_experts page,
+// MoonEPExperts.apply: padding rows past the last segment come out zero).
+__global__ __launch_bounds__(256) void k_zero_tail(uint16_t* out, const int32_t* status, int NvS, int H) {
+  const int first = status[1];
+  const int row = blockIdx.x;
+  if (row < first || row >= NvS) return;
+  for (int h = threadIdx.x * 8; h < H; h += 256 * 8) *(u32x4*)(out + (size_t)row * H + h) = u32x4{0u, 0u, 0u, 0u};
+}
+
+}  // namespace moe

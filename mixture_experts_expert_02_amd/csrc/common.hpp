@@ -1,0 +1,78 @@
+// Shared device helpers for the gfx950 MoE experts kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 with round-to-nearest-even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ float sigmoidf_fast(float x) {
+  return 1.0f / (1.0f + __expf(-x));
+}
+
+// Activation of the gate/up pair, in fp32.
+//   act 0: silu(g) * u                       (moonep_experts page, module docstring)
+//   act 1: SwiGLU-OAI, g' = min(g, limit), u' = clamp(u, -limit, limit),
+//          g' * sigmoid(alpha g') * (u' + beta)   (trtllm_mxfp4_moe page,
+//          TrtLlmMxfp4ExpertsBase parameters; formula is the gpt-oss reading)
+struct ActParams {
+  int32_t kind;
+  float alpha, beta, limit;
+};
+
+__device__ __forceinline__ float gated_act(const ActParams& a, float g, float u) {
+  if (a.kind == 0) return g * sigmoidf_fast(g) * u;
+  g = fminf(g, a.limit);
+  u = fminf(fmaxf(u, -a.limit), a.limit);
+  return g * sigmoidf_fast(a.alpha * g) * (u + a.beta);
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const uint32_t lane = __lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Mask of the lanes of this wave whose key equals this lane's key. Every lane
+// of the wave must call it (keys of idle lanes should be a sentinel).
+__device__ __forceinline__ uint64_t match_key(int key, int nbits) {
+  uint64_t m = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    const int bit = (key >> b) & 1;
+    const uint64_t s = __ballot(bit);
+    m &= bit ? s : ~s;
+  }
+  return m;
+}
+
+// Hardware dispatches workgroup b to XCD (b mod 8). Renumber so that
+// consecutive logical ids run on the same XCD and share its L2.
+// nblk must be a multiple of 8.
+__device__ __forceinline__ int xcd_logical_block(int b, int nblk) {
+  return (b & 7) * (nblk >> 3) + (b >> 3);
+}
+
+}  // namespace moe

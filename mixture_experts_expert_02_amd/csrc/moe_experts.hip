@@ -1,0 +1,432 @@
+// Host side of the MoE experts library: argument checks, workspace layout,
+// kernel launch sequence. Exports the C ABI declared in include/moe_experts.h.
+//
+// Launch sequence of a token-major forward, all on the caller's stream, no
+// host synchronisation and no device reads on the host:
+//   align (1 or 3 kernels) -> GEMM1 (+ activation x route weight) -> GEMM2 -> combine
+// The GEMM grids are sized on the host from upper bounds (rows / BM + segments);
+// workgroups past the device-side tile count exit at once, so no readback is needed.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/moe_experts.h"
+#include "align.hpp"
+#include "combine.hpp"
+#include "gemm_bf16.hpp"
+#include "gemm_skinny.hpp"
+
+namespace {
+
+constexpr int kMaxExperts = 4096;
+constexpr int kFusedMaxRows = 4096;
+constexpr int kFusedMaxExperts = 1024;
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+int bits_for(int E) {  // bits needed for keys 0..E
+  int b = 0;
+  while ((1 << b) <= E) ++b;
+  return b;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Decode-shaped problems (few rows per weight row) and all MXFP4 problems use
+// the weight-streaming kernels; the rest the LDS-tiled MFMA kernels.
+bool use_skinny(const moe_problem& p, long long rows) {
+  return p.wfmt == MOE_W_MXFP4 || rows <= 32LL * p.E;
+}
+
+struct Plan {
+  long long M;   // rows (T*k, or NvS)
+  bool skinny;
+  int BM;
+  int mt_cap;
+  bool fused_align;
+  int chunk, nch;
+  // byte offsets
+  size_t status, counts, cu, offsets, tile_seg, tile_row0, blkcnt, blkbad, perm, inv_perm, w_sorted, act,
+      y, total;
+};
+
+int check_problem(const moe_problem* p, bool grouped) {
+  if (!p) return MOE_EINVAL;
+  if (p->T < 0 || p->H <= 0 || p->I <= 0 || p->E <= 0) return MOE_EINVAL;
+  if (!grouped && (p->k <= 0 || p->k > p->E)) return MOE_EINVAL;
+  if (p->wfmt != MOE_W_BF16 && p->wfmt != MOE_W_MXFP4) return MOE_EINVAL;
+  if (p->act != MOE_ACT_SILU && p->act != MOE_ACT_SWIGLU_OAI) return MOE_EINVAL;
+  if (p->act == MOE_ACT_SWIGLU_OAI) {
+    if (!std::isfinite(p->alpha) || !std::isfinite(p->beta) || std::isnan(p->limit)) return MOE_EINVAL;
+    if (!(p->limit > 0.f)) return MOE_ENOTSUP;
+  }
+  if (p->H % 64 || p->I % 64) return MOE_ENOTSUP;
+  if (p->E > kMaxExperts) return MOE_ENOTSUP;
+  const long long rows = grouped ? (long long)p->T : (long long)p->T * p->k;
+  if (rows > (1LL << 30)) return MOE_ENOTSUP;
+  return MOE_OK;
+}
+
+Plan make_plan(const moe_problem& p, bool grouped) {
+  Plan pl{};
+  pl.M = grouped ? (long long)p.T : (long long)p.T * p.k;
+  pl.skinny = use_skinny(p, pl.M);
+  pl.BM = pl.skinny ? moe::skinny::BM : moe::big::BM;
+  pl.mt_cap = ceil_div(pl.M, pl.BM) + (int)std::min<long long>(p.E, pl.M);
+  pl.fused_align = !grouped && pl.M <= kFusedMaxRows && p.E <= kFusedMaxExperts;
+  if (!grouped && !pl.fused_align) {
+    pl.chunk = (int)std::max<long long>(512, (ceil_div(pl.M, 256) + 63) / 64 * 64);
+    pl.nch = ceil_div(pl.M, pl.chunk);
+  }
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = up(o + bytes);
+    return at;
+  };
+  pl.status = take(16);
+  pl.counts = take(4ull * p.E);
+  pl.cu = take(4ull * p.E);
+  pl.offsets = take(4ull * p.E);
+  pl.tile_seg = take(4ull * std::max(pl.mt_cap, 1));
+  pl.tile_row0 = take(4ull * std::max(pl.mt_cap, 1));
+  if (!grouped) {
+    if (!pl.fused_align) {
+      pl.blkcnt = take(4ull * pl.nch * p.E);
+      pl.blkbad = take(4ull * pl.nch);
+    }
+    pl.perm = take(4ull * pl.M);
+    pl.inv_perm = take(4ull * pl.M);
+    pl.w_sorted = take(4ull * pl.M);
+  }
+  pl.act = take(2ull * pl.M * p.I);
+  if (!grouped) pl.y = take(2ull * pl.M * p.H);
+  pl.total = o;
+  return pl;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return (T*)((char*)base + off);
+}
+
+moe::ActParams act_params(const moe_problem& p) {
+  moe::ActParams a;
+  a.kind = p.act;
+  a.alpha = p.alpha;
+  a.beta = p.beta;
+  a.limit = p.limit;
+  return a;
+}
+
+int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// ---------------------------------------------------------------- align
+int launch_align(const int32_t* ids, const float* w, int M, int E, int BM, const Plan& pl, moe::AlignOut o,
+                 void* ws, hipStream_t s) {
+  const int nbits = bits_for(E);
+  if (pl.fused_align) {
+    const size_t lds = (size_t)(7 * E + 16) * 4;
+    hipLaunchKernelGGL(moe::k_align_fused, dim3(1), dim3(256), lds, s, ids, w, M, E, nbits, BM, o);
+    return launch_status();
+  }
+  int32_t* blkcnt = at<int32_t>(ws, pl.blkcnt);
+  int32_t* blkbad = at<int32_t>(ws, pl.blkbad);
+  const int nblk = ceil_div(pl.nch, 4);
+  const size_t lds4 = (size_t)4 * E * 4;
+  hipLaunchKernelGGL(moe::k_align_count, dim3(nblk), dim3(256), lds4, s, ids, M, E, nbits, pl.chunk, pl.nch,
+                     blkcnt, blkbad);
+  hipLaunchKernelGGL(moe::k_align_scan, dim3(1), dim3(1024), (size_t)(3 * E + 32) * 4, s, blkcnt,
+                     (const int32_t*)blkbad, pl.nch, M, E, BM, o);
+  hipLaunchKernelGGL(moe::k_align_scatter, dim3(nblk), dim3(256), lds4, s, ids, w, M, E, nbits, pl.chunk,
+                     pl.nch, (const int32_t*)blkcnt, o);
+  return launch_status();
+}
+
+bool g_attr_done = false;
+int set_attrs() {
+  if (g_attr_done) return MOE_OK;
+  hipError_t e = hipSuccess;
+  e = hipFuncSetAttribute((const void*)moe::k_align_count, hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute((const void*)moe::k_align_scatter, hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
+  if (e != hipSuccess) return MOE_EHIP;
+  g_attr_done = true;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- GEMMs
+struct GemmIO {
+  const void* A;
+  const int32_t* a_perm;
+  int a_div;
+  const void* B0;
+  const void* B1;
+  const uint8_t* S0;
+  const uint8_t* S1;
+  int N, K;
+  void* C;
+  const float* row_w;
+};
+
+template <bool GATED>
+int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws, hipStream_t s) {
+  const int32_t* tile_seg = at<int32_t>(ws, pl.tile_seg);
+  const int32_t* tile_row0 = at<int32_t>(ws, pl.tile_row0);
+  const int32_t* cu = at<int32_t>(ws, pl.cu);
+  const int32_t* status = at<int32_t>(ws, pl.status);
+  if (pl.skinny) {
+    moe::skinny::Params q;
+    q.A = (const uint16_t*)io.A;
+    q.a_perm = io.a_perm;
+    q.a_div = io.a_div;
+    q.B0 = io.B0;
+    q.B1 = io.B1;
+    q.S0 = io.S0;
+    q.S1 = io.S1;
+    q.N = io.N;
+    q.K = io.K;
+    q.tile_seg = tile_seg;
+    q.tile_row0 = tile_row0;
+    q.seg_end = cu;
+    q.status = status;
+    q.mt_cap = pl.mt_cap;
+    q.n_tiles = ceil_div(io.N, moe::skinny::NW * moe::skinny::WN);
+    q.C = (uint16_t*)io.C;
+    q.row_w = io.row_w;
+    q.act = act_params(p);
+    const dim3 grid((unsigned)pl.mt_cap * q.n_tiles);
+    if (p.wfmt == MOE_W_MXFP4)
+      hipLaunchKernelGGL((moe::skinny::k_gemm<moe::skinny::W_MXFP4, GATED>), grid, dim3(moe::skinny::NT), 0, s, q);
+    else
+      hipLaunchKernelGGL((moe::skinny::k_gemm<moe::skinny::W_BF16, GATED>), grid, dim3(moe::skinny::NT), 0, s, q);
+  } else {
+    moe::big::Params q;
+    q.A = (const uint16_t*)io.A;
+    q.a_perm = io.a_perm;
+    q.a_div = io.a_div;
+    q.B0 = (const uint16_t*)io.B0;
+    q.B1 = (const uint16_t*)io.B1;
+    q.N = io.N;
+    q.K = io.K;
+    q.tile_seg = tile_seg;
+    q.tile_row0 = tile_row0;
+    q.seg_end = cu;
+    q.status = status;
+    q.mt_cap = pl.mt_cap;
+    q.n_tiles = ceil_div(io.N, GATED ? moe::big::BN / 2 : moe::big::BN);
+    q.C = (uint16_t*)io.C;
+    q.row_w = io.row_w;
+    q.act = act_params(p);
+    const long long groups = ceil_div(q.n_tiles, moe::big::GN);
+    long long nblk = groups * pl.mt_cap * moe::big::GN;
+    nblk = (nblk + 7) / 8 * 8;
+    if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
+    hipLaunchKernelGGL((moe::big::k_gemm<GATED>), dim3((unsigned)nblk), dim3(moe::big::NT), 0, s, q);
+  }
+  return launch_status();
+}
+
+int check_common_ptrs(const moe_problem* p, const void* x, const void* wg, const void* wu, const void* wd,
+                      const uint8_t* sg, const uint8_t* su, const uint8_t* sd, const void* out, const void* ws) {
+  if (!x || !wg || !wu || !wd || !out || !ws) return MOE_EINVAL;
+  if (p->wfmt == MOE_W_MXFP4 && (!sg || !su || !sd)) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(wg) || !aligned16(wu) || !aligned16(wd) || !aligned16(out)) return MOE_EINVAL;
+  if (((uintptr_t)ws % kAlign) != 0) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const float* tw, const void* wg,
+                 const void* wu, const void* wd, const uint8_t* sg, const uint8_t* su, const uint8_t* sd,
+                 void* out, void* ws, size_t ws_bytes, hipStream_t s, void* const* ev, int n_ev) {
+  int rc = check_problem(p, false);
+  if (rc) return rc;
+  if (!ids || !tw) return MOE_EINVAL;
+  rc = check_common_ptrs(p, x, wg, wu, wd, sg, su, sd, out, ws);
+  if (rc) return rc;
+  if (n_ev != 0 && (n_ev != 5 || !ev)) return MOE_EINVAL;
+  if (p->T == 0) return MOE_OK;
+  const Plan pl = make_plan(*p, false);
+  if (ws_bytes < pl.total) return MOE_ENOSPC;
+  if ((rc = set_attrs())) return rc;
+  auto mark = [&](int i) {
+    if (n_ev) hipEventRecord((hipEvent_t)ev[i], s);
+  };
+
+  moe::AlignOut o;
+  o.counts = at<int32_t>(ws, pl.counts);
+  o.cu = at<int32_t>(ws, pl.cu);
+  o.offsets = at<int32_t>(ws, pl.offsets);
+  o.perm = at<int32_t>(ws, pl.perm);
+  o.inv_perm = at<int32_t>(ws, pl.inv_perm);
+  o.w_sorted = at<float>(ws, pl.w_sorted);
+  o.tile_seg = at<int32_t>(ws, pl.tile_seg);
+  o.tile_row0 = at<int32_t>(ws, pl.tile_row0);
+  o.status = at<int32_t>(ws, pl.status);
+  const int M = (int)pl.M;
+
+  mark(0);
+  if ((rc = launch_align(ids, tw, M, p->E, pl.BM, pl, o, ws, s))) return rc;
+
+  GemmIO g1{x, o.perm, p->k, wg, wu, sg, su, p->I, p->H, at<void>(ws, pl.act), o.w_sorted};
+  mark(1);
+  if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
+
+  GemmIO g2{at<void>(ws, pl.act), nullptr, 1, wd, nullptr, sd, nullptr, p->H, p->I, at<void>(ws, pl.y), nullptr};
+  mark(2);
+  if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
+
+  mark(3);
+  hipLaunchKernelGGL(moe::k_combine, dim3(p->T), dim3(256), 0, s, at<const uint16_t>(ws, pl.y),
+                     (const int32_t*)o.inv_perm, p->T, p->k, p->H, (uint16_t*)out);
+  mark(4);
+  return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_experts_workspace_bytes(const moe_problem* p) {
+  if (check_problem(p, false)) return 0;
+  return make_plan(*p, false).total;
+}
+
+int moe_experts_workspace_layout(const moe_problem* p, moe_ws_layout* l) {
+  if (!l || check_problem(p, false)) return MOE_EINVAL;
+  const Plan pl = make_plan(*p, false);
+  l->status = pl.status;
+  l->counts = pl.counts;
+  l->cu_seqlens = pl.cu;
+  l->perm = pl.perm;
+  l->inv_perm = pl.inv_perm;
+  l->w_sorted = pl.w_sorted;
+  l->act = pl.act;
+  l->y = pl.y;
+  l->total = pl.total;
+  return MOE_OK;
+}
+
+int moe_experts_forward(const moe_problem* p, const void* x, const int32_t* topk_ids, const float* topk_weights,
+                        const void* w_gate, const void* w_up, const void* w_down, const uint8_t* s_gate,
+                        const uint8_t* s_up, const uint8_t* s_down, void* out, void* workspace,
+                        size_t workspace_bytes, moe_stream_t stream) {
+  return forward_impl(p, x, topk_ids, topk_weights, w_gate, w_up, w_down, s_gate, s_up, s_down, out, workspace,
+                      workspace_bytes, (hipStream_t)stream, nullptr, 0);
+}
+
+int moe_experts_forward_timed(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                              const float* topk_weights, const void* w_gate, const void* w_up, const void* w_down,
+                              const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down, void* out,
+                              void* workspace, size_t workspace_bytes, moe_stream_t stream,
+                              void* const* stage_events, int n_events) {
+  return forward_impl(p, x, topk_ids, topk_weights, w_gate, w_up, w_down, s_gate, s_up, s_down, out, workspace,
+                      workspace_bytes, (hipStream_t)stream, stage_events, n_events);
+}
+
+size_t moe_align_workspace_bytes(int32_t T, int32_t k, int32_t E) {
+  moe_problem p{};
+  p.T = T;
+  p.H = 64;
+  p.I = 64;
+  p.E = E;
+  p.k = k;
+  if (check_problem(&p, false)) return 0;
+  Plan pl = make_plan(p, false);
+  // align needs the tables and chunk counters, not perm / act / y
+  return pl.perm;
+}
+
+int moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts, int32_t* cu_seqlens,
+              int32_t* perm, int32_t* inv_perm, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  moe_problem p{};
+  p.T = T;
+  p.H = 64;
+  p.I = 64;
+  p.E = E;
+  p.k = k;
+  int rc = check_problem(&p, false);
+  if (rc) return rc;
+  if (!topk_ids || !counts || !cu_seqlens || !perm || !inv_perm || !workspace) return MOE_EINVAL;
+  if (((uintptr_t)workspace % kAlign) != 0) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  const Plan pl = make_plan(p, false);
+  if (workspace_bytes < pl.perm) return MOE_ENOSPC;
+  if ((rc = set_attrs())) return rc;
+  moe::AlignOut o;
+  o.counts = counts;
+  o.cu = cu_seqlens;
+  o.offsets = at<int32_t>(workspace, pl.offsets);
+  o.perm = perm;
+  o.inv_perm = inv_perm;
+  o.w_sorted = nullptr;
+  o.tile_seg = at<int32_t>(workspace, pl.tile_seg);
+  o.tile_row0 = at<int32_t>(workspace, pl.tile_row0);
+  o.status = at<int32_t>(workspace, pl.status);
+  return launch_align(topk_ids, nullptr, (int)pl.M, E, pl.BM, pl, o, workspace, (hipStream_t)stream);
+}
+
+size_t moe_experts_grouped_workspace_bytes(const moe_problem* p) {
+  if (check_problem(p, true)) return 0;
+  return make_plan(*p, true).total;
+}
+
+int moe_experts_forward_grouped(const moe_problem* p, const void* x_nvs, const int32_t* cu_seqlens,
+                                const float* route_w, const void* w_gate, const void* w_up, const void* w_down,
+                                const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down, void* out_nvs,
+                                void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  int rc = check_problem(p, true);
+  if (rc) return rc;
+  if (!cu_seqlens || !route_w) return MOE_EINVAL;
+  rc = check_common_ptrs(p, x_nvs, w_gate, w_up, w_down, s_gate, s_up, s_down, out_nvs, workspace);
+  if (rc) return rc;
+  if (p->T == 0) return MOE_OK;
+  const Plan pl = make_plan(*p, true);
+  if (workspace_bytes < pl.total) return MOE_ENOSPC;
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = workspace;
+  moe::AlignOut o{};
+  o.counts = at<int32_t>(ws, pl.counts);
+  o.cu = at<int32_t>(ws, pl.cu);
+  o.offsets = at<int32_t>(ws, pl.offsets);
+  o.tile_seg = at<int32_t>(ws, pl.tile_seg);
+  o.tile_row0 = at<int32_t>(ws, pl.tile_row0);
+  o.status = at<int32_t>(ws, pl.status);
+  hipLaunchKernelGGL(moe::k_grouped_prep, dim3(1), dim3(1024), (size_t)(3 * p->E + 32) * 4, s, cu_seqlens, p->E,
+                     p->T, pl.BM, o);
+  if ((rc = launch_status())) return rc;
+  GemmIO g1{x_nvs, nullptr, 1, w_gate, w_up, s_gate, s_up, p->I, p->H, at<void>(ws, pl.act), route_w};
+  if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
+  GemmIO g2{at<void>(ws, pl.act), nullptr, 1, w_down, nullptr, s_down, nullptr, p->H, p->I, out_nvs, nullptr};
+  if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
+  hipLaunchKernelGGL(moe::k_zero_tail, dim3(p->T), dim3(256), 0, s, (uint16_t*)out_nvs,
+                     (const int32_t*)o.status, p->T, p->H);
+  return launch_status();
+}
+
+int moe_device_error(const void* workspace, int32_t* n_bad) {
+  if (!workspace || !n_bad) return MOE_EINVAL;
+  // status word sits at offset 0 of every workspace layout
+  const hipError_t e = hipMemcpy(n_bad, workspace, sizeof(int32_t), hipMemcpyDeviceToHost);
+  return e == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "success";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_ENOTSUP: return "unsupported problem";
+    case MOE_ENOSPC: return "workspace too small";
+    case MOE_EHIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -30,8 +30,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
 }
 
+// 1 / (1 + e^-x) with v_exp_f32 and v_rcp_f32 (about 1 ulp each); for very
+// negative x the reciprocal of +inf is 0, so x * sigmoid(x) stays finite.
 __device__ __forceinline__ float sigmoidf_fast(float x) {
-  return 1.0f / (1.0f + __expf(-x));
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
 // Activation of the gate/up pair, in fp32.

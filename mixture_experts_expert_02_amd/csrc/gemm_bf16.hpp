@@ -7,16 +7,16 @@
 // activation times the per-row route weight in its epilogue (module docstring:
 // the route weight is applied to the activation); GEMM2 is the down projection.
 //
-// Tile: 256 rows x 256 weight rows x 64 K per stage, 4 waves (one per SIMD),
+// Tile: 256 rows x 256 weight rows, 32 K per stage, 4 waves (one per SIMD),
 // each wave a 128 x 128 block of v_mfma_f32_32x32x16_bf16 results. For GEMM1
 // the 256 weight rows are 128 gate rows and the same 128 up rows, so each
 // wave holds gate and up accumulators for the same 128 x 64 outputs. Both
 // operands go from HBM straight into LDS with global_load_lds_dwordx4 (no
-// staging registers), double buffered (2 x 64 KB), with the 16-byte chunks of
-// every row XOR-swizzled by (row & 7) so that the MFMA operand reads are
-// bank-conflict free. In a partial row tile the rows
+// staging registers) through five 32 KB stages (all 160 KB of LDS), so loads
+// run four stages ahead of the MFMAs; the 16-byte chunks of every row are XOR-swizzled so
+// that the MFMA operand reads are bank-conflict free. In a partial row tile the rows
 // past the segment end load a valid row of the tile and their results are
-// dropped; a wave whose 128 rows are all past the end skips its MFMAs.
+// dropped.
 #pragma once
 
 #include "common.hpp"
@@ -26,9 +26,11 @@ namespace big {
 
 constexpr int BM = 256;  // rows per tile
 constexpr int BN = 256;  // weight rows per tile (GEMM1: 128 gate + 128 up)
-constexpr int BK = 64;   // K per stage
+constexpr int BK = 32;   // K per stage
+constexpr int NS = 5;    // LDS stages (loads run NS-1 stages ahead); 5 x 32 KB = all 160 KB
 constexpr int NT = 256;  // threads
 constexpr int GN = 8;    // n-tiles per tile group (L2 locality of concurrently running tiles)
+constexpr int STAGE_U4 = BM * BK / 8;  // 16-byte slots per operand per stage (16 KB)
 
 struct Params {
   const uint16_t* A;       // rows [*, K] bf16
@@ -48,27 +50,54 @@ struct Params {
   ActParams act;
 };
 
-__device__ __forceinline__ int lds_chunk(int row, int chunk) {  // in 16-byte units
-  return row * (BK / 8) + (chunk ^ (row & 7));
+// A stage holds 256 rows x 32 K (64 bytes = four 16-byte chunks per row) of
+// A, then the same of B. Chunk c of row r sits in slot c ^ ((r >> 2) & 3):
+// ds_read_b128 serves 16 lanes per pass from a 256-byte bank window, and the
+// 16 consecutive rows one MFMA operand read touches fall on 16 distinct
+// 16-byte banks.
+__device__ __forceinline__ int lds_slot(int row, int chunk) {
+  return row * (BK / 8) + (chunk ^ ((row >> 2) & 3));
 }
 
-// One wave-wide direct-to-LDS load: 64 lanes x 16 bytes into the 1 KB LDS
-// block at lds_block (rows r0..r0+7 of a tile, r0 a multiple of 8). Lane l
-// fills the block's 16-byte slot l, i.e. row r0 + l/8, slot l%8, which under
-// the swizzle holds global chunk (l%8) ^ (l/8) of that row.
-__device__ __forceinline__ void load_block_to_lds(const uint16_t* __restrict__ gbase, uint32_t elem_off,
-                                                  u32x4* lds_block) {
-  __builtin_amdgcn_global_load_lds(gbase + elem_off, lds_block, 16, 0, 0);
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// Workgroup barrier without a memory fence. __syncthreads() would make the
+// compiler wait for every outstanding direct-to-LDS load (vmcnt(0)), which
+// cancels the loads running ahead; instead each wave first waits (vmcnt(N))
+// for the stage about to be read, then meets the others here. The "memory"
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(N); gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// (7 = no wait) in 6:4, lgkmcnt (15 = no wait) in 11:8.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+// MFMA operand reads are inline-asm ds_read_b128: the compiler's wait-count
+// pass would otherwise put a vmcnt(0) in front of every LDS read because it
+// cannot tell the stage being read from the stages still being filled by
+// direct-to-LDS loads. The reads are then completed by an explicit
+// lgkmcnt(0) that also names the destination registers, so nothing uses them
+// earlier. The reads of one k-substep share an address register; the
+// per-fragment row offsets go in the immediate field.
+#define MOE_LGKM_WAIT_TIE(a, b)                                                                \
+  asm volatile("s_waitcnt lgkmcnt(0)"                                                          \
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), \
+                 "+v"(b[3]))
 
 template <bool GATED>
 __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
-  // two stages, each its own LDS object
-  __shared__ u32x4 sA0[BM * BK / 8], sA1[BM * BK / 8];
-  __shared__ u32x4 sB0[BN * BK / 8], sB1[BN * BK / 8];
+  // NS stages of [A 16 KB | B 16 KB]
+  __shared__ u32x4 smem[NS * 2 * STAGE_U4];
+  constexpr uint32_t STAGE_BYTES = 2 * STAGE_U4 * 16;
+  constexpr uint32_t B_HALF = STAGE_U4 * 16;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA targets go in M0
 
   // block -> (row tile, column tile): groups of GN column tiles, row tiles
   // inside a group, column tile fastest; logical ids contiguous per XCD
@@ -86,41 +115,55 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   const int N = p.N, K = p.K;
   const int n0 = nt * (GATED ? BN / 2 : BN);
 
-  // ---- load assignment: wave w fills the 1 KB blocks w*8 .. w*8+7 of the A
-  // tile and of the B tile (rows w*64 .. w*64+63). 32-bit element offsets:
-  // the host keeps T*H, M*I and N*K below 2^31.
-  const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;
-  const uint16_t* __restrict__ Ab = p.A;
-  const uint16_t* __restrict__ B0b = p.B0 + (size_t)seg * N * K;
-  const uint16_t* __restrict__ B1b = GATED ? p.B1 + (size_t)seg * N * K : B0b;
-  uint32_t a_off[8], b_off[8];
+  // ---- direct-to-LDS load assignment. One wave instruction fills a 1 KB LDS
+  // block = 16 rows of a stage; lane l writes slot l of it, i.e. row l/4,
+  // slot l%4, which holds global chunk (l%4) ^ ((row >> 2) & 3). Wave w fills
+  // blocks 4w..4w+3 (rows 64w..64w+63) of the A and of the B half.
+  // 32-bit byte offsets: the host keeps T*H, M*I and N*K below 2^31 elements.
+  const int lrow = lane >> 2;
+  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const char* __restrict__ Ab = (const char*)p.A;
+  const char* __restrict__ B0b = (const char*)(p.B0 + (size_t)seg * N * K);
+  const char* __restrict__ B1b = GATED ? (const char*)(p.B1 + (size_t)seg * N * K) : B0b;
+  uint32_t a_off[4], b_off[4];
   {
     const int first = p.a_perm ? p.a_perm[row0] / p.a_div : row0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wave * 64 + i * 8 + lrow;
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave * 64 + i * 16 + lrow;
       int arow = first;
       if (r < rows) arow = p.a_perm ? p.a_perm[row0 + r] / p.a_div : row0 + r;
-      a_off[i] = (uint32_t)arow * (uint32_t)K + lchunk * 8;
+      a_off[i] = ((uint32_t)arow * (uint32_t)K + lchunk * 8) * 2u;
       const int n = min(n0 + (GATED ? (r & 127) : r), N - 1);
-      b_off[i] = (uint32_t)n * (uint32_t)K + lchunk * 8;
+      b_off[i] = ((uint32_t)n * (uint32_t)K + lchunk * 8) * 2u;
     }
   }
-  // In GEMM1, rows 0..127 of the B tile are gate rows (waves 0, 1) and rows
+  // In GEMM1, rows 0..127 of the B half are gate rows (waves 0, 1) and rows
   // 128..255 up rows (waves 2, 3).
-  const uint16_t* __restrict__ Bw = (GATED && wave >= 2) ? B1b : B0b;
+  const char* __restrict__ Bw = (GATED && wave >= 2) ? B1b : B0b;
 
-#define MOE_BIG_ISSUE(sA_, sB_, k0)                                          \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i) {                            \
-    load_block_to_lds(Ab, a_off[i] + (k0), &sA_[(wave * 8 + i) * 64]);       \
-    load_block_to_lds(Bw, b_off[i] + (k0), &sB_[(wave * 8 + i) * 64]);       \
+  // one direct-to-LDS load: q = 0..3 A rows 16q.., q = 4..7 B rows 16(q-4)..
+#define MOE_BIG_DMA(st, kbytes, q)                                                                           \
+  {                                                                                                          \
+    const int qq = (q) & 3;                                                                                  \
+    if ((q) < 4)                                                                                             \
+      __builtin_amdgcn_global_load_lds(Ab + (a_off[qq] + (kbytes)),                                          \
+                                       &smem[(st) * 2 * STAGE_U4 + (wave * 4 + qq) * 64], 16, 0, 0);          \
+    else                                                                                                     \
+      __builtin_amdgcn_global_load_lds(Bw + (b_off[qq] + (kbytes)),                                          \
+                                       &smem[(st) * 2 * STAGE_U4 + STAGE_U4 + (wave * 4 + qq) * 64], 16, 0, 0); \
   }
 
-  // ---- wave tile
+  // ---- wave tile: 128 rows x 128 weight rows
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lk = lane >> 5;
-  const bool active = rows > wm * 128;  // wave has rows of this tile
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u32x4*)smem;
+  uint32_t a_lane[2], b_lane[2];  // per k-substep byte address of fragment 0 inside a stage
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    a_lane[ks] = lds0 + 16u * lds_slot(wm * 128 + lr, ks * 2 + lk);
+    b_lane[ks] = lds0 + B_HALF + 16u * lds_slot((GATED ? wn * 64 : wn * 128) + lr, ks * 2 + lk);
+  }
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -130,70 +173,158 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-#define MOE_BIG_COMPUTE(sA_, sB_)                                                                        \
-  if (active) {                                                                                          \
-    _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks) {                                             \
-      const int ch = ks * 2 + lk;                                                                        \
-      bf16x8 af[4], bfr[4];                                                                              \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                    \
-        const int R = wm * 128 + i * 32 + lr;                                                            \
-        af[i] = *(const bf16x8*)&sA_[lds_chunk(R, ch)];                                                  \
-      }                                                                                                  \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                    \
-        const int R = GATED ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + lr) : (wn * 128 + j * 32 + lr); \
-        bfr[j] = *(const bf16x8*)&sB_[lds_chunk(R, ch)];                                                 \
-      }                                                                                                  \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                      \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                    \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);      \
-    }                                                                                                    \
+  bf16x8 fa[4], fb[4], ga[4], gb[4];
+  // One fragment read: q = 0..3 A fragment q (rows +32 q, 2048 bytes apart),
+  // q = 4..7 B fragment q-4 (GEMM1: gate rows 0, 32, up rows 128, 160, i.e.
+  // 0, 2048, 8192, 10240 bytes; GEMM2: rows +32 (q-4)).
+#define MOE_DSR(d, addr, off) asm volatile("ds_read_b128 %0, %1 offset:" #off : "=v"(d) : "v"(addr))
+#define MOE_BIG_READ1(dA, dB, st, ks, q)                                 \
+  {                                                                      \
+    const uint32_t aa = a_lane[ks] + (uint32_t)(st) * STAGE_BYTES;       \
+    const uint32_t bb = b_lane[ks] + (uint32_t)(st) * STAGE_BYTES;       \
+    switch (q) {                                                         \
+      case 0: MOE_DSR(dA[0], aa, 0); break;                              \
+      case 1: MOE_DSR(dA[1], aa, 2048); break;                           \
+      case 2: MOE_DSR(dA[2], aa, 4096); break;                           \
+      case 3: MOE_DSR(dA[3], aa, 6144); break;                           \
+      case 4: MOE_DSR(dB[0], bb, 0); break;                              \
+      case 5: MOE_DSR(dB[1], bb, 2048); break;                           \
+      case 6: if (GATED) MOE_DSR(dB[2], bb, 8192); else MOE_DSR(dB[2], bb, 4096); break;   \
+      default: if (GATED) MOE_DSR(dB[3], bb, 10240); else MOE_DSR(dB[3], bb, 6144); break; \
+    }                                                                    \
   }
-
-  // vmcnt(0): this wave's direct-to-LDS loads have landed; the barrier then
-  // publishes every wave's loads and retires the reads of the other stage.
-#define MOE_BIG_SYNC()                               \
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   \
-  __syncthreads();
+  // MFMAs 2k, 2k+1 of a 16-MFMA batch (A fragment k/2, B fragments 2(k%2), +1)
+#define MOE_BIG_MFMA2(dA, dB, k)                                                                      \
+  {                                                                                                   \
+    const int i_ = (k) >> 1, j_ = ((k) & 1) * 2;                                                      \
+    acc[i_][j_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA[i_], dB[j_], acc[i_][j_], 0, 0, 0);       \
+    acc[i_][j_ + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA[i_], dB[j_ + 1], acc[i_][j_ + 1], 0, 0, 0); \
+  }
 
   const int KT = K / BK;
-  MOE_BIG_ISSUE(sA0, sB0, 0)
-  MOE_BIG_SYNC()
-  for (int kt = 0; kt < KT; kt += 2) {
-    if (kt + 1 < KT) { MOE_BIG_ISSUE(sA1, sB1, (kt + 1) * BK) }
-    MOE_BIG_COMPUTE(sA0, sB0)
-    MOE_BIG_SYNC()
-    if (kt + 1 >= KT) break;
-    if (kt + 2 < KT) { MOE_BIG_ISSUE(sA0, sB0, (kt + 2) * BK) }
-    MOE_BIG_COMPUTE(sA1, sB1)
-    MOE_BIG_SYNC()
+  // prologue: stages 0..NS-2 in flight, wait for stage 0
+#pragma unroll
+  for (int st0 = 0; st0 < NS - 1; ++st0) {
+    if (st0 < KT) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) MOE_BIG_DMA(st0, (uint32_t)st0 * BK * 2u, q)
+    }
   }
-#undef MOE_BIG_ISSUE
-#undef MOE_BIG_COMPUTE
-#undef MOE_BIG_SYNC
+  {
+    const int ahead = min(NS - 2, KT - 1);
+    if (ahead >= 3) wait_vmcnt<24>();
+    else if (ahead == 2) wait_vmcnt<16>();
+    else if (ahead == 1) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
+  }
+  stage_barrier();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) MOE_BIG_READ1(fa, fb, 0, 0, q)
+
+  // One stage s (buffer st = s mod NS), 32 MFMAs in two batches of 16:
+  //   batch (s,0): each MFMA pair goes with one read of fragments (s,1) and
+  //     every other pair with one load of stage s+NS-1 (into the buffer of
+  //     stage s-1, which every wave finished reading before the last barrier);
+  //   wait for fragments (s,1): this wave is done reading stage s;
+  //   wait until stage s+1 has landed, barrier;
+  //   batch (s,1): each MFMA pair with one read of fragments (s+1,0), every
+  //     other pair with one more load of stage s+NS-1.
+  // A wave issues instructions in order and has its SIMD to itself, so an
+  // MFMA that waits behind a run of loads leaves the matrix unit idle; spread
+  // out, the loads and reads issue in the shadow of the MFMAs.
+  // Odd waves issue their loads one MFMA pair later than even waves, so at
+  // most two waves' loads queue at the load unit at once.
+  const int odd = wave & 1;
+  int st = 0;
+  for (int s = 0; s < KT; ++s) {
+    const int stn = st + 1 == NS ? 0 : st + 1;
+    const int stl = st == 0 ? NS - 1 : st - 1;
+    const bool load = s + NS - 1 < KT;
+    const uint32_t kl = (uint32_t)(s + NS - 1) * BK * 2u;
+    MOE_LGKM_WAIT_TIE(fa, fb);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (load && (k & 1) == odd) MOE_BIG_DMA(stl, kl, k >> 1)
+      MOE_BIG_READ1(ga, gb, st, 1, k)
+      MOE_BIG_MFMA2(fa, fb, k)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    MOE_LGKM_WAIT_TIE(ga, gb);
+    const bool next = s + 1 < KT;
+    if (next) {
+      // loads still allowed in flight: full stages after s+1, plus the four
+      // loads of stage s+NS-1 issued above
+      const int full = max(0, min(s + NS - 2, KT - 1) - (s + 1));
+      if (load) wait_vmcnt<8 * (NS - 3) + 4>();
+      else if (full >= 2) wait_vmcnt<16>();
+      else if (full == 1) wait_vmcnt<8>();
+      else wait_vmcnt<0>();
+      stage_barrier();
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (load && (k & 1) == odd) MOE_BIG_DMA(stl, kl, 4 + (k >> 1))
+      if (next) MOE_BIG_READ1(fa, fb, stn, 0, k)
+      MOE_BIG_MFMA2(ga, gb, k)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    st = stn;
+  }
+#undef MOE_BIG_DMA
+#undef MOE_DSR
+#undef MOE_BIG_READ1
+#undef MOE_BIG_MFMA2
 
   // ---- epilogue. 32x32 result layout: lane holds column (lane & 31) and, in
-  // register r, row 8 (r / 4) + 4 (lane / 32) + (r % 4).
-  if (!active) return;
+  // register r, row 8 (r / 4) + 4 (lane / 32) + (r % 4). A wave whose 128 rows
+  // are all past the segment end has computed on copies of a valid row (its
+  // own SIMD, so no cost to the others) and stores nothing.
+  if (rows <= wm * 128) return;
+  // Results go through LDS so that every lane stores 16 contiguous bytes.
+  // Each wave stages in its own stage buffer, none of them the last stage's
+  // (other waves may still read that one); all other buffers were retired by
+  // the last barrier, so no barrier is needed here. 128 rows x 64 columns per
+  // pass, rows padded to 72 elements against bank conflicts.
+  constexpr int LDR = 72;
+  uint16_t* sc = (uint16_t*)&smem[((KT + wave) % NS) * 2 * STAGE_U4];
+  const int wrows = min(128, rows - wm * 128);
+  const int wrow0 = row0 + wm * 128;
+  const int cc = lane & 7;          // 16-byte chunk of a staged row
+  const int rr = lane >> 3;         // staged row within a group of 8
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int pass = 0; pass < (GATED ? 1 : 2); ++pass) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * 128 + i * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
-      if (row >= rows) continue;
-      uint16_t* crow = p.C + (size_t)(row0 + row) * N;
-      if (GATED) {
-        const float w = p.row_w[row0 + row];
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = n0 + wn * 64 + j * 32 + lr;
-          if (n < N) crow[n] = f32_to_bf16_rne(gated_act(p.act, acc[i][j][r], acc[i][j + 2][r]) * w);
+      for (int rq = 0; rq < 4; ++rq) {
+        const int rbase = i * 32 + rq * 8 + lk * 4;  // 4 consecutive rows r = rq*4 + 0..3
+        float w4[4] = {1.f, 1.f, 1.f, 1.f};
+        if (GATED) {
+#pragma unroll
+          for (int r3 = 0; r3 < 4; ++r3)
+            if (rbase + r3 < wrows) w4[r3] = p.row_w[wrow0 + rbase + r3];
         }
-      } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 128 + j * 32 + lr;
-          if (n < N) crow[n] = f32_to_bf16_rne(acc[i][j][r]);
+        for (int r3 = 0; r3 < 4; ++r3) {
+          const int r = rq * 4 + r3;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float v;
+            if (GATED) v = gated_act(p.act, acc[i][j][r], acc[i][j + 2][r]) * w4[r3];
+            else v = acc[i][2 * pass + j][r];
+            const __bf16 h = (__bf16)v;
+            sc[(rbase + r3) * LDR + j * 32 + lr] = *(const uint16_t*)&h;
+          }
         }
+      }
+    }
+    const int col0 = n0 + (GATED ? wn * 64 : wn * 128 + pass * 64) + cc * 8;
+    if (col0 < N) {
+#pragma unroll 4
+      for (int t = 0; t < 16; ++t) {
+        const int row = t * 8 + rr;
+        if (row < wrows)
+          *(u32x4*)(p.C + (size_t)(wrow0 + row) * N + col0) = *(const u32x4*)&sc[row * LDR + cc * 8];
       }
     }
   }

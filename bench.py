@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--print-source-hash", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -82,6 +83,38 @@ def make_inputs(wl, dev):
     else:
         W, S = synth.make_bf16_weights(wl, device=dev), (None, None, None)
     return x, torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev), W, S, ids, w
+
+
+def kernel_source_hash() -> str:
+    """sha256 of the sources the prefill and decode GEMMs are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("common.hpp", "gemm_bf16.hpp", "gemm_skinny.hpp"):
+        with open(os.path.join(ROOT, "mixture_experts_expert_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary
+    of this workload: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled
+    by what the same counter read for a 1 GiB device copy. None when there is
+    no summary or the GEMM sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"gemm1_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    copy_bytes = float(kv["copy_bytes"])
+    f_scale = copy_bytes / (float(kv["copy_fetch_kib"]) * 1024.0)
+    w_scale = copy_bytes / (float(kv["copy_write_kib"]) * 1024.0)
+    return (float(kv["gemm1_fetch_kib"]) * 1024.0 * f_scale + float(kv["gemm1_write_kib"]) * 1024.0 * w_scale)
 
 
 def touched_weight_bytes(wl, ids):
@@ -132,6 +165,9 @@ def cpu_baseline(wl, x, ids, w, W, S, n_tokens):
 
 def main():
     args = parse()
+    if args.print_source_hash:
+        print(kernel_source_hash())
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the experts step "
               f"holds every expert on a single MI355X.", file=sys.stderr)
@@ -196,7 +232,9 @@ def main():
         g1_flops = 4.0 * M * wl.H * wl.I
         achieved = g1_flops / (avg["gemm1"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "gemm1 (gate+up, bf16)"}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": counter_traffic(wl.name),
+                "kernel": "gemm1 (gate+up, bf16)",
+                "algorithmic_bytes": n_touched * 2 * wl.I * wl.H * 2 + M * wl.H * 2 + M * wl.I * 2}
     else:
         metric = METRIC
         unit = "GB/s"
@@ -204,7 +242,8 @@ def main():
         g1_bytes = n_touched * 2 * wl.H * wl.I * (0.5 + 1 / 32)
         achieved = g1_bytes / (avg["gemm1"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "gemm1 (gate+up, MXFP4)"}
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic(wl.name),
+                "kernel": "gemm1 (gate+up, MXFP4)", "algorithmic_bytes": g1_bytes}
 
     res = {
         "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,

@@ -7,16 +7,20 @@
 // activation times the per-row route weight in its epilogue (module docstring:
 // the route weight is applied to the activation); GEMM2 is the down projection.
 //
-// Tile: 256 rows x 256 weight rows, 32 K per stage, 4 waves (one per SIMD),
-// each wave a 128 x 128 block of v_mfma_f32_32x32x16_bf16 results. For GEMM1
-// the 256 weight rows are 128 gate rows and the same 128 up rows, so each
-// wave holds gate and up accumulators for the same 128 x 64 outputs. Both
-// operands go from HBM straight into LDS with global_load_lds_dwordx4 (no
-// staging registers) through five 32 KB stages (all 160 KB of LDS), so loads
-// run four stages ahead of the MFMAs; the 16-byte chunks of every row are XOR-swizzled so
-// that the MFMA operand reads are bank-conflict free. In a partial row tile the rows
-// past the segment end load a valid row of the tile and their results are
-// dropped.
+// Tile: 256 rows x 256 weight rows, 32 K per stage, 8 waves (two per SIMD),
+// each wave a 128 x 64 block of v_mfma_f32_32x32x16_bf16 results (128 fp32
+// accumulators per lane, so two waves fit a SIMD's registers). For GEMM1 the
+// 256 weight rows are 128 gate rows and the same 128 up rows, and each wave
+// holds gate and up accumulators for the same 128 x 32 outputs. A wave issues
+// in order, so a lone wave whose load, LDS read or barrier stalls leaves its
+// SIMD's matrix unit idle; with two waves per SIMD one issues MFMAs while the
+// other waits. Both operands go from HBM straight into LDS with
+// global_load_lds_dwordx4 (no staging registers) through five 32 KB stages
+// (all 160 KB of LDS), so loads run four stages ahead of the MFMAs; the
+// 16-byte chunks of every row are XOR-swizzled so that the MFMA operand reads
+// are bank-conflict free. In a partial row tile the rows past the segment end
+// load a valid row of the tile and their results are dropped; waves whose
+// 128 rows are all past the end skip their MFMAs.
 #pragma once
 
 #include "common.hpp"
@@ -28,7 +32,7 @@ constexpr int BM = 256;  // rows per tile
 constexpr int BN = 256;  // weight rows per tile (GEMM1: 128 gate + 128 up)
 constexpr int BK = 32;   // K per stage
 constexpr int NS = 5;    // LDS stages (loads run NS-1 stages ahead); 5 x 32 KB = all 160 KB
-constexpr int NT = 256;  // threads
+constexpr int NT = 512;  // threads (8 waves)
 constexpr int GN = 8;    // n-tiles per tile group (L2 locality of concurrently running tiles)
 constexpr int STAGE_U4 = BM * BK / 8;  // 16-byte slots per operand per stage (16 KB)
 
@@ -85,8 +89,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // per-fragment row offsets go in the immediate field.
 #define MOE_LGKM_WAIT_TIE(a, b)                                                                \
   asm volatile("s_waitcnt lgkmcnt(0)"                                                          \
-               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), \
-                 "+v"(b[3]))
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]))
 
 template <bool GATED>
 __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
@@ -118,19 +121,19 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   // ---- direct-to-LDS load assignment. One wave instruction fills a 1 KB LDS
   // block = 16 rows of a stage; lane l writes slot l of it, i.e. row l/4,
   // slot l%4, which holds global chunk (l%4) ^ ((row >> 2) & 3). Wave w fills
-  // blocks 4w..4w+3 (rows 64w..64w+63) of the A and of the B half.
+  // blocks 2w, 2w+1 (rows 32w..32w+31) of the A and of the B half.
   // 32-bit byte offsets: the host keeps T*H, M*I and N*K below 2^31 elements.
   const int lrow = lane >> 2;
   const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
   const char* __restrict__ Ab = (const char*)p.A;
   const char* __restrict__ B0b = (const char*)(p.B0 + (size_t)seg * N * K);
   const char* __restrict__ B1b = GATED ? (const char*)(p.B1 + (size_t)seg * N * K) : B0b;
-  uint32_t a_off[4], b_off[4];
+  uint32_t a_off[2], b_off[2];
   {
     const int first = p.a_perm ? p.a_perm[row0] / p.a_div : row0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wave * 64 + i * 16 + lrow;
+    for (int i = 0; i < 2; ++i) {
+      const int r = wave * 32 + i * 16 + lrow;
       int arow = first;
       if (r < rows) arow = p.a_perm ? p.a_perm[row0 + r] / p.a_div : row0 + r;
       a_off[i] = ((uint32_t)arow * (uint32_t)K + lchunk * 8) * 2u;
@@ -138,45 +141,50 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
       b_off[i] = ((uint32_t)n * (uint32_t)K + lchunk * 8) * 2u;
     }
   }
-  // In GEMM1, rows 0..127 of the B half are gate rows (waves 0, 1) and rows
-  // 128..255 up rows (waves 2, 3).
-  const char* __restrict__ Bw = (GATED && wave >= 2) ? B1b : B0b;
+  // In GEMM1, rows 0..127 of the B half are gate rows (waves 0-3) and rows
+  // 128..255 up rows (waves 4-7).
+  const char* __restrict__ Bw = (GATED && wave >= 4) ? B1b : B0b;
 
-  // one direct-to-LDS load: q = 0..3 A rows 16q.., q = 4..7 B rows 16(q-4)..
+  // one direct-to-LDS load: q = 0, 1 A rows 32w + 16q..; q = 2, 3 B rows
 #define MOE_BIG_DMA(st, kbytes, q)                                                                           \
   {                                                                                                          \
-    const int qq = (q) & 3;                                                                                  \
-    if ((q) < 4)                                                                                             \
+    const int qq = (q) & 1;                                                                                  \
+    if ((q) < 2)                                                                                             \
       __builtin_amdgcn_global_load_lds(Ab + (a_off[qq] + (kbytes)),                                          \
-                                       &smem[(st) * 2 * STAGE_U4 + (wave * 4 + qq) * 64], 16, 0, 0);          \
+                                       &smem[(st) * 2 * STAGE_U4 + (wave * 2 + qq) * 64], 16, 0, 0);          \
     else                                                                                                     \
       __builtin_amdgcn_global_load_lds(Bw + (b_off[qq] + (kbytes)),                                          \
-                                       &smem[(st) * 2 * STAGE_U4 + STAGE_U4 + (wave * 4 + qq) * 64], 16, 0, 0); \
+                                       &smem[(st) * 2 * STAGE_U4 + STAGE_U4 + (wave * 2 + qq) * 64], 16, 0, 0); \
   }
 
-  // ---- wave tile: 128 rows x 128 weight rows
-  const int wm = wave >> 1, wn = wave & 1;
+  // ---- wave tile: 128 rows x 64 weight rows (GEMM1: 32 gate + the same 32 up)
+  const int wm = wave >> 2, wn = wave & 3;
+  // Waves 4-7 (rows 128..255) have nothing to do in a tile of at most 128
+  // rows (the last tile of a segment); they share their SIMDs with waves 0-3,
+  // which then get the matrix units to themselves. They still load and meet
+  // the barriers.
+  const bool active = rows > wm * 128;
   const int lr = lane & 31, lk = lane >> 5;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u32x4*)smem;
   uint32_t a_lane[2], b_lane[2];  // per k-substep byte address of fragment 0 inside a stage
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     a_lane[ks] = lds0 + 16u * lds_slot(wm * 128 + lr, ks * 2 + lk);
-    b_lane[ks] = lds0 + B_HALF + 16u * lds_slot((GATED ? wn * 64 : wn * 128) + lr, ks * 2 + lk);
+    b_lane[ks] = lds0 + B_HALF + 16u * lds_slot((GATED ? wn * 32 : wn * 64) + lr, ks * 2 + lk);
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  bf16x8 fa[4], fb[4], ga[4], gb[4];
+  bf16x8 fa[4], fb[2], ga[4], gb[2];
   // One fragment read: q = 0..3 A fragment q (rows +32 q, 2048 bytes apart),
-  // q = 4..7 B fragment q-4 (GEMM1: gate rows 0, 32, up rows 128, 160, i.e.
-  // 0, 2048, 8192, 10240 bytes; GEMM2: rows +32 (q-4)).
+  // q = 4, 5 B fragment q-4 (GEMM1: gate rows 0, up rows +128, i.e. 0 and
+  // 8192 bytes; GEMM2: rows +32 (q-4)).
 #define MOE_DSR(d, addr, off) asm volatile("ds_read_b128 %0, %1 offset:" #off : "=v"(d) : "v"(addr))
 #define MOE_BIG_READ1(dA, dB, st, ks, q)                                 \
   {                                                                      \
@@ -188,17 +196,14 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
       case 2: MOE_DSR(dA[2], aa, 4096); break;                           \
       case 3: MOE_DSR(dA[3], aa, 6144); break;                           \
       case 4: MOE_DSR(dB[0], bb, 0); break;                              \
-      case 5: MOE_DSR(dB[1], bb, 2048); break;                           \
-      case 6: if (GATED) MOE_DSR(dB[2], bb, 8192); else MOE_DSR(dB[2], bb, 4096); break;   \
-      default: if (GATED) MOE_DSR(dB[3], bb, 10240); else MOE_DSR(dB[3], bb, 6144); break; \
+      default: if (GATED) MOE_DSR(dB[1], bb, 8192); else MOE_DSR(dB[1], bb, 2048); break; \
     }                                                                    \
   }
-  // MFMAs 2k, 2k+1 of a 16-MFMA batch (A fragment k/2, B fragments 2(k%2), +1)
-#define MOE_BIG_MFMA2(dA, dB, k)                                                                      \
-  {                                                                                                   \
-    const int i_ = (k) >> 1, j_ = ((k) & 1) * 2;                                                      \
-    acc[i_][j_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA[i_], dB[j_], acc[i_][j_], 0, 0, 0);       \
-    acc[i_][j_ + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA[i_], dB[j_ + 1], acc[i_][j_ + 1], 0, 0, 0); \
+  // MFMAs 2k, 2k+1 of an 8-MFMA batch (A fragment k, B fragments 0 and 1)
+#define MOE_BIG_MFMA2(dA, dB, k)                                                                    \
+  if (active) {                                                                                     \
+    acc[k][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA[k], dB[0], acc[k][0], 0, 0, 0);          \
+    acc[k][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA[k], dB[1], acc[k][1], 0, 0, 0);          \
   }
 
   const int KT = K / BK;
@@ -207,34 +212,27 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   for (int st0 = 0; st0 < NS - 1; ++st0) {
     if (st0 < KT) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) MOE_BIG_DMA(st0, (uint32_t)st0 * BK * 2u, q)
+      for (int q = 0; q < 4; ++q) MOE_BIG_DMA(st0, (uint32_t)st0 * BK * 2u, q)
     }
   }
   {
     const int ahead = min(NS - 2, KT - 1);
-    if (ahead >= 3) wait_vmcnt<24>();
-    else if (ahead == 2) wait_vmcnt<16>();
-    else if (ahead == 1) wait_vmcnt<8>();
+    if (ahead >= 3) wait_vmcnt<12>();
+    else if (ahead == 2) wait_vmcnt<8>();
+    else if (ahead == 1) wait_vmcnt<4>();
     else wait_vmcnt<0>();
   }
   stage_barrier();
 #pragma unroll
-  for (int q = 0; q < 8; ++q) MOE_BIG_READ1(fa, fb, 0, 0, q)
+  for (int q = 0; q < 6; ++q) MOE_BIG_READ1(fa, fb, 0, 0, q)
 
-  // One stage s (buffer st = s mod NS), 32 MFMAs in two batches of 16:
-  //   batch (s,0): each MFMA pair goes with one read of fragments (s,1) and
-  //     every other pair with one load of stage s+NS-1 (into the buffer of
-  //     stage s-1, which every wave finished reading before the last barrier);
+  // One stage s (buffer st = s mod NS), 16 MFMAs in two batches of 8:
+  //   batch (s,0): the six reads of fragments (s,1) and two loads of stage
+  //     s+NS-1 (into the buffer of stage s-1, which every wave finished
+  //     reading before the last barrier) between its MFMA pairs;
   //   wait for fragments (s,1): this wave is done reading stage s;
   //   wait until stage s+1 has landed, barrier;
-  //   batch (s,1): each MFMA pair with one read of fragments (s+1,0), every
-  //     other pair with one more load of stage s+NS-1.
-  // A wave issues instructions in order and has its SIMD to itself, so an
-  // MFMA that waits behind a run of loads leaves the matrix unit idle; spread
-  // out, the loads and reads issue in the shadow of the MFMAs.
-  // Odd waves issue their loads one MFMA pair later than even waves, so at
-  // most two waves' loads queue at the load unit at once.
-  const int odd = wave & 1;
+  //   batch (s,1): the six reads of fragments (s+1,0) and the other two loads.
   int st = 0;
   for (int s = 0; s < KT; ++s) {
     const int stn = st + 1 == NS ? 0 : st + 1;
@@ -243,28 +241,32 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
     const uint32_t kl = (uint32_t)(s + NS - 1) * BK * 2u;
     MOE_LGKM_WAIT_TIE(fa, fb);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (load && (k & 1) == odd) MOE_BIG_DMA(stl, kl, k >> 1)
+    for (int k = 0; k < 4; ++k) {
+      if (load && (k & 1) == 0) MOE_BIG_DMA(stl, kl, k >> 1)
       MOE_BIG_READ1(ga, gb, st, 1, k)
+      if (k < 2) MOE_BIG_READ1(ga, gb, st, 1, 4 + k)
       MOE_BIG_MFMA2(fa, fb, k)
       __builtin_amdgcn_sched_barrier(0);
     }
     MOE_LGKM_WAIT_TIE(ga, gb);
     const bool next = s + 1 < KT;
     if (next) {
-      // loads still allowed in flight: full stages after s+1, plus the four
+      // loads still allowed in flight: full stages after s+1, plus the two
       // loads of stage s+NS-1 issued above
       const int full = max(0, min(s + NS - 2, KT - 1) - (s + 1));
-      if (load) wait_vmcnt<8 * (NS - 3) + 4>();
-      else if (full >= 2) wait_vmcnt<16>();
-      else if (full == 1) wait_vmcnt<8>();
+      if (load) wait_vmcnt<4 * (NS - 3) + 2>();
+      else if (full >= 2) wait_vmcnt<8>();
+      else if (full == 1) wait_vmcnt<4>();
       else wait_vmcnt<0>();
       stage_barrier();
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (load && (k & 1) == odd) MOE_BIG_DMA(stl, kl, 4 + (k >> 1))
-      if (next) MOE_BIG_READ1(fa, fb, stn, 0, k)
+    for (int k = 0; k < 4; ++k) {
+      if (load && (k & 1) == 0) MOE_BIG_DMA(stl, kl, 2 + (k >> 1))
+      if (next) {
+        MOE_BIG_READ1(fa, fb, stn, 0, k)
+        if (k < 2) MOE_BIG_READ1(fa, fb, stn, 0, 4 + k)
+      }
       MOE_BIG_MFMA2(ga, gb, k)
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -276,21 +278,19 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
 #undef MOE_BIG_MFMA2
 
   // ---- epilogue. 32x32 result layout: lane holds column (lane & 31) and, in
-  // register r, row 8 (r / 4) + 4 (lane / 32) + (r % 4). A wave whose 128 rows
-  // are all past the segment end has computed on copies of a valid row (its
-  // own SIMD, so no cost to the others) and stores nothing.
-  if (rows <= wm * 128) return;
+  // register r, row 8 (r / 4) + 4 (lane / 32) + (r % 4).
+  if (!active) return;
   // Results go through LDS so that every lane stores 16 contiguous bytes.
-  // Each wave stages in its own stage buffer, none of them the last stage's
-  // (other waves may still read that one); all other buffers were retired by
-  // the last barrier, so no barrier is needed here. 128 rows x 64 columns per
-  // pass, rows padded to 72 elements against bank conflicts.
-  constexpr int LDR = 72;
-  uint16_t* sc = (uint16_t*)&smem[((KT + wave) % NS) * 2 * STAGE_U4];
+  // Waves 2b, 2b+1 stage in halves of one stage buffer, none of them the last
+  // stage's (other waves may still read that one); all other buffers were
+  // retired by the last barrier, so no barrier is needed here. 128 rows x 32
+  // columns per pass, rows padded to 40 elements against bank conflicts.
+  constexpr int LDR = 40;
+  uint16_t* sc = (uint16_t*)&smem[((KT + (wave >> 1)) % NS) * 2 * STAGE_U4 + (wave & 1) * STAGE_U4];
   const int wrows = min(128, rows - wm * 128);
   const int wrow0 = row0 + wm * 128;
-  const int cc = lane & 7;          // 16-byte chunk of a staged row
-  const int rr = lane >> 3;         // staged row within a group of 8
+  const int cc = lane & 3;          // 16-byte chunk of a staged 64-byte row
+  const int rr = lane >> 2;         // staged row within a group of 16
 #pragma unroll
   for (int pass = 0; pass < (GATED ? 1 : 2); ++pass) {
 #pragma unroll
@@ -307,22 +307,19 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
 #pragma unroll
         for (int r3 = 0; r3 < 4; ++r3) {
           const int r = rq * 4 + r3;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            float v;
-            if (GATED) v = gated_act(p.act, acc[i][j][r], acc[i][j + 2][r]) * w4[r3];
-            else v = acc[i][2 * pass + j][r];
-            const __bf16 h = (__bf16)v;
-            sc[(rbase + r3) * LDR + j * 32 + lr] = *(const uint16_t*)&h;
-          }
+          float v;
+          if (GATED) v = gated_act(p.act, acc[i][0][r], acc[i][1][r]) * w4[r3];
+          else v = acc[i][pass][r];
+          const __bf16 h = (__bf16)v;
+          sc[(rbase + r3) * LDR + lr] = *(const uint16_t*)&h;
         }
       }
     }
-    const int col0 = n0 + (GATED ? wn * 64 : wn * 128 + pass * 64) + cc * 8;
+    const int col0 = n0 + (GATED ? wn * 32 : wn * 64 + pass * 32) + cc * 8;
     if (col0 < N) {
 #pragma unroll 4
-      for (int t = 0; t < 16; ++t) {
-        const int row = t * 8 + rr;
+      for (int t = 0; t < 8; ++t) {
+        const int row = t * 16 + rr;
         if (row < wrows)
           *(u32x4*)(p.C + (size_t)(wrow0 + row) * N + col0) = *(const u32x4*)&sc[row * LDR + cc * 8];
       }

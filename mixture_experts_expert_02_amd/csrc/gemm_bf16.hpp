@@ -33,7 +33,6 @@ constexpr int BN = 256;  // weight rows per tile (GEMM1: 128 gate + 128 up)
 constexpr int BK = 32;   // K per stage
 constexpr int NS = 5;    // LDS stages (loads run NS-1 stages ahead); 5 x 32 KB = all 160 KB
 constexpr int NT = 512;  // threads (8 waves)
-constexpr int GN = 8;    // n-tiles per tile group (L2 locality of concurrently running tiles)
 constexpr int STAGE_U4 = BM * BK / 8;  // 16-byte slots per operand per stage (16 KB)
 
 struct Params {
@@ -49,6 +48,8 @@ struct Params {
   const int32_t* status;   // status[2] = number of row tiles
   int32_t mt_cap;          // row tiles the grid covers
   int32_t n_tiles;         // column tiles
+  int32_t gn;              // column tiles per tile group
+  int32_t xcd_remap;       // 1: renumber workgroups so consecutive tiles share an XCD
   uint16_t* C;             // [rows, N] bf16 output, sorted row order
   const float* row_w;      // GEMM1: route weight per sorted row
   ActParams act;
@@ -102,14 +103,15 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA targets go in M0
 
-  // block -> (row tile, column tile): groups of GN column tiles, row tiles
-  // inside a group, column tile fastest; logical ids contiguous per XCD
-  const int L = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int span = p.mt_cap * GN;
+  // block -> (row tile, column tile): groups of gn column tiles, row tiles
+  // inside a group, column tile fastest; optionally logical ids contiguous
+  // per XCD so that tiles sharing weight and row panels share an L2
+  const int L = p.xcd_remap ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  const int span = p.mt_cap * p.gn;
   const int grp = L / span;
   const int r_in = L - grp * span;
-  const int mt = r_in / GN;
-  const int nt = grp * GN + (r_in - mt * GN);
+  const int mt = r_in / p.gn;
+  const int nt = grp * p.gn + (r_in - mt * p.gn);
   if (nt >= p.n_tiles || mt >= p.status[2]) return;
 
   const int seg = p.tile_seg[mt];

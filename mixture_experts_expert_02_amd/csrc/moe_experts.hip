@@ -225,8 +225,10 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     q.C = (uint16_t*)io.C;
     q.row_w = io.row_w;
     q.act = act_params(p);
-    const long long groups = ceil_div(q.n_tiles, moe::big::GN);
-    long long nblk = groups * pl.mt_cap * moe::big::GN;
+    q.gn = std::min(q.n_tiles, 2);
+    q.xcd_remap = 1;
+    const long long groups = ceil_div(q.n_tiles, q.gn);
+    long long nblk = groups * pl.mt_cap * q.gn;
     nblk = (nblk + 7) / 8 * 8;
     if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
     hipLaunchKernelGGL((moe::big::k_gemm<GATED>), dim3((unsigned)nblk), dim3(moe::big::NT), 0, s, q);

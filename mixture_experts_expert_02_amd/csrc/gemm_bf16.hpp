@@ -7,7 +7,7 @@
 // activation times the per-row route weight in its epilogue (module docstring:
 // the route weight is applied to the activation); GEMM2 is the down projection.
 //
-// Tile: 256 rows x 256 weight rows, 32 K per stage, 8 waves (two per SIMD),
+// Tile: 256 rows x 256 weight rows, 64 K per stage, 8 waves (two per SIMD),
 // each wave a 128 x 64 block of v_mfma_f32_32x32x16_bf16 results (128 fp32
 // accumulators per lane, so two waves fit a SIMD's registers). For GEMM1 the
 // 256 weight rows are 128 gate rows and the same 128 up rows, and each wave
@@ -15,10 +15,13 @@
 // in order, so a lone wave whose load, LDS read or barrier stalls leaves its
 // SIMD's matrix unit idle; with two waves per SIMD one issues MFMAs while the
 // other waits. Both operands go from HBM straight into LDS with
-// global_load_lds_dwordx4 (no staging registers) through five 32 KB stages
-// (all 160 KB of LDS), so loads run four stages ahead of the MFMAs; the
-// 16-byte chunks of every row are XOR-swizzled so that the MFMA operand reads
-// are bank-conflict free. In a partial row tile the rows past the segment end
+// global_load_lds_dwordx4 (no staging registers) through two 64 KB stages:
+// the loads of stage s+1 run under the MFMAs of stage s. Only vmcnt(0)
+// reliably orders the completion of direct-to-LDS loads, so a wave waits for
+// all of its loads before each stage barrier; 64 K per stage keeps the
+// barriers and the load instructions per MFMA few. The 16-byte chunks of
+// every row are XOR-swizzled so that the MFMA operand reads are bank-conflict
+// free. In a partial row tile the rows past the segment end
 // load a valid row of the tile and their results are dropped; waves whose
 // 128 rows are all past the end skip their MFMAs.
 #pragma once
@@ -30,10 +33,11 @@ namespace big {
 
 constexpr int BM = 256;  // rows per tile
 constexpr int BN = 256;  // weight rows per tile (GEMM1: 128 gate + 128 up)
-constexpr int BK = 32;   // K per stage
-constexpr int NS = 5;    // LDS stages (loads run NS-1 stages ahead); 5 x 32 KB = all 160 KB
+constexpr int BK = 64;   // K per stage
+constexpr int NS = 2;    // LDS stages: the loads of stage s+1 run during stage s
 constexpr int NT = 512;  // threads (8 waves)
-constexpr int STAGE_U4 = BM * BK / 8;  // 16-byte slots per operand per stage (16 KB)
+constexpr int STAGE_U4 = BM * BK / 8;  // 16-byte slots per operand per stage (32 KB)
+constexpr int KS = BK / 16;            // MFMA k-substeps per stage
 
 struct Params {
   const uint16_t* A;       // rows [*, K] bf16
@@ -55,13 +59,13 @@ struct Params {
   ActParams act;
 };
 
-// A stage holds 256 rows x 32 K (64 bytes = four 16-byte chunks per row) of
-// A, then the same of B. Chunk c of row r sits in slot c ^ ((r >> 2) & 3):
-// ds_read_b128 serves 16 lanes per pass from a 256-byte bank window, and the
-// 16 consecutive rows one MFMA operand read touches fall on 16 distinct
-// 16-byte banks.
+// A stage holds 256 rows x 64 K (128 bytes = eight 16-byte chunks per row)
+// of A, then the same of B. Chunk c of row r sits in slot c ^ ((r >> 1) & 7):
+// ds_read_b128 serves 16 lanes per pass from a 256-byte bank window (two
+// rows), and the 16 consecutive rows one MFMA operand read touches fall on 16
+// distinct 16-byte banks.
 __device__ __forceinline__ int lds_slot(int row, int chunk) {
-  return row * (BK / 8) + (chunk ^ ((row >> 2) & 3));
+  return row * (BK / 8) + (chunk ^ ((row >> 1) & 7));
 }
 
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -94,7 +98,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <bool GATED>
 __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
-  // NS stages of [A 16 KB | B 16 KB]
+  // NS stages of [A 32 KB | B 32 KB]
   __shared__ u32x4 smem[NS * 2 * STAGE_U4];
   constexpr uint32_t STAGE_BYTES = 2 * STAGE_U4 * 16;
   constexpr uint32_t B_HALF = STAGE_U4 * 16;
@@ -121,42 +125,41 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   const int n0 = nt * (GATED ? BN / 2 : BN);
 
   // ---- direct-to-LDS load assignment. One wave instruction fills a 1 KB LDS
-  // block = 16 rows of a stage; lane l writes slot l of it, i.e. row l/4,
-  // slot l%4, which holds global chunk (l%4) ^ ((row >> 2) & 3). Wave w fills
-  // blocks 2w, 2w+1 (rows 32w..32w+31) of the A and of the B half.
+  // block = 8 rows of a stage; lane l writes slot l of it, i.e. row l/8, slot
+  // l%8, which holds global chunk (l%8) ^ ((row >> 1) & 7). Wave w fills
+  // blocks 4w..4w+3 (rows 32w..32w+31) of the A and of the B half.
   // 32-bit byte offsets: the host keeps T*H, M*I and N*K below 2^31 elements.
-  const int lrow = lane >> 2;
-  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
   const char* __restrict__ Ab = (const char*)p.A;
   const char* __restrict__ B0b = (const char*)(p.B0 + (size_t)seg * N * K);
   const char* __restrict__ B1b = GATED ? (const char*)(p.B1 + (size_t)seg * N * K) : B0b;
-  uint32_t a_off[2], b_off[2];
+  uint32_t a_off[4], b_off[4];
   {
     const int first = p.a_perm ? p.a_perm[row0] / p.a_div : row0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = wave * 32 + i * 16 + lrow;
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave * 32 + i * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((r >> 1) & 7);
       int arow = first;
       if (r < rows) arow = p.a_perm ? p.a_perm[row0 + r] / p.a_div : row0 + r;
-      a_off[i] = ((uint32_t)arow * (uint32_t)K + lchunk * 8) * 2u;
+      a_off[i] = ((uint32_t)arow * (uint32_t)K + chunk * 8) * 2u;
       const int n = min(n0 + (GATED ? (r & 127) : r), N - 1);
-      b_off[i] = ((uint32_t)n * (uint32_t)K + lchunk * 8) * 2u;
+      b_off[i] = ((uint32_t)n * (uint32_t)K + chunk * 8) * 2u;
     }
   }
   // In GEMM1, rows 0..127 of the B half are gate rows (waves 0-3) and rows
   // 128..255 up rows (waves 4-7).
   const char* __restrict__ Bw = (GATED && wave >= 4) ? B1b : B0b;
 
-  // one direct-to-LDS load: q = 0, 1 A rows 32w + 16q..; q = 2, 3 B rows
+  // one direct-to-LDS load: q = 0..3 A rows 32w + 8q..; q = 4..7 B rows
 #define MOE_BIG_DMA(st, kbytes, q)                                                                           \
   {                                                                                                          \
-    const int qq = (q) & 1;                                                                                  \
-    if ((q) < 2)                                                                                             \
+    const int qq = (q) & 3;                                                                                  \
+    if ((q) < 4)                                                                                             \
       __builtin_amdgcn_global_load_lds(Ab + (a_off[qq] + (kbytes)),                                          \
-                                       &smem[(st) * 2 * STAGE_U4 + (wave * 2 + qq) * 64], 16, 0, 0);          \
+                                       &smem[(st) * 2 * STAGE_U4 + (wave * 4 + qq) * 64], 16, 0, 0);          \
     else                                                                                                     \
       __builtin_amdgcn_global_load_lds(Bw + (b_off[qq] + (kbytes)),                                          \
-                                       &smem[(st) * 2 * STAGE_U4 + STAGE_U4 + (wave * 2 + qq) * 64], 16, 0, 0); \
+                                       &smem[(st) * 2 * STAGE_U4 + STAGE_U4 + (wave * 4 + qq) * 64], 16, 0, 0); \
   }
 
   // ---- wave tile: 128 rows x 64 weight rows (GEMM1: 32 gate + the same 32 up)
@@ -168,9 +171,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   const bool active = rows > wm * 128;
   const int lr = lane & 31, lk = lane >> 5;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u32x4*)smem;
-  uint32_t a_lane[2], b_lane[2];  // per k-substep byte address of fragment 0 inside a stage
+  uint32_t a_lane[KS], b_lane[KS];  // per k-substep byte address of fragment 0 inside a stage
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     a_lane[ks] = lds0 + 16u * lds_slot(wm * 128 + lr, ks * 2 + lk);
     b_lane[ks] = lds0 + B_HALF + 16u * lds_slot((GATED ? wn * 32 : wn * 64) + lr, ks * 2 + lk);
   }
@@ -184,9 +187,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   bf16x8 fa[4], fb[2], ga[4], gb[2];
-  // One fragment read: q = 0..3 A fragment q (rows +32 q, 2048 bytes apart),
+  // One fragment read: q = 0..3 A fragment q (rows +32 q, 4096 bytes apart),
   // q = 4, 5 B fragment q-4 (GEMM1: gate rows 0, up rows +128, i.e. 0 and
-  // 8192 bytes; GEMM2: rows +32 (q-4)).
+  // 16384 bytes; GEMM2: rows +32 (q-4)).
 #define MOE_DSR(d, addr, off) asm volatile("ds_read_b128 %0, %1 offset:" #off : "=v"(d) : "v"(addr))
 #define MOE_BIG_READ1(dA, dB, st, ks, q)                                 \
   {                                                                      \
@@ -194,11 +197,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
     const uint32_t bb = b_lane[ks] + (uint32_t)(st) * STAGE_BYTES;       \
     switch (q) {                                                         \
       case 0: MOE_DSR(dA[0], aa, 0); break;                              \
-      case 1: MOE_DSR(dA[1], aa, 2048); break;                           \
-      case 2: MOE_DSR(dA[2], aa, 4096); break;                           \
-      case 3: MOE_DSR(dA[3], aa, 6144); break;                           \
+      case 1: MOE_DSR(dA[1], aa, 4096); break;                           \
+      case 2: MOE_DSR(dA[2], aa, 8192); break;                           \
+      case 3: MOE_DSR(dA[3], aa, 12288); break;                          \
       case 4: MOE_DSR(dB[0], bb, 0); break;                              \
-      default: if (GATED) MOE_DSR(dB[1], bb, 8192); else MOE_DSR(dB[1], bb, 2048); break; \
+      default: if (GATED) MOE_DSR(dB[1], bb, 16384); else MOE_DSR(dB[1], bb, 4096); break; \
     }                                                                    \
   }
   // MFMAs 2k, 2k+1 of an 8-MFMA batch (A fragment k, B fragments 0 and 1)
@@ -207,70 +210,61 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
     acc[k][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA[k], dB[0], acc[k][0], 0, 0, 0);          \
     acc[k][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA[k], dB[1], acc[k][1], 0, 0, 0);          \
   }
+  // one k-substep: MFMAs on (cA, cB) interleaved with the reads of the next
+  // fragments (nA, nB) from stage buffer nst, substep nks, and with four of
+  // this wave's loads of the next stage (q0..q0+3 when dma)
+#define MOE_BIG_SUBSTEP(cA, cB, nA, nB, nst, nks, rd, dma, q0)                  \
+  {                                                                              \
+    MOE_LGKM_WAIT_TIE(cA, cB);                                                   \
+    _Pragma("unroll") for (int k = 0; k < 4; ++k) {                              \
+      if (dma) MOE_BIG_DMA(stn, kl, (q0) + k)                                   \
+      if (rd) {                                                                  \
+        MOE_BIG_READ1(nA, nB, nst, nks, k)                                       \
+        if (k < 2) MOE_BIG_READ1(nA, nB, nst, nks, 4 + k)                        \
+      }                                                                          \
+      MOE_BIG_MFMA2(cA, cB, k)                                                   \
+      __builtin_amdgcn_sched_barrier(0);                                         \
+    }                                                                            \
+  }
 
   const int KT = K / BK;
-  // prologue: stages 0..NS-2 in flight, wait for stage 0
+  // prologue: stage 0
 #pragma unroll
-  for (int st0 = 0; st0 < NS - 1; ++st0) {
-    if (st0 < KT) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) MOE_BIG_DMA(st0, (uint32_t)st0 * BK * 2u, q)
-    }
-  }
-  {
-    const int ahead = min(NS - 2, KT - 1);
-    if (ahead >= 3) wait_vmcnt<12>();
-    else if (ahead == 2) wait_vmcnt<8>();
-    else if (ahead == 1) wait_vmcnt<4>();
-    else wait_vmcnt<0>();
-  }
+  for (int q = 0; q < 8; ++q) MOE_BIG_DMA(0, 0u, q)
+  wait_vmcnt<0>();
   stage_barrier();
 #pragma unroll
   for (int q = 0; q < 6; ++q) MOE_BIG_READ1(fa, fb, 0, 0, q)
 
-  // One stage s (buffer st = s mod NS), 16 MFMAs in two batches of 8:
-  //   batch (s,0): the six reads of fragments (s,1) and two loads of stage
-  //     s+NS-1 (into the buffer of stage s-1, which every wave finished
-  //     reading before the last barrier) between its MFMA pairs;
-  //   wait for fragments (s,1): this wave is done reading stage s;
-  //   wait until stage s+1 has landed, barrier;
-  //   batch (s,1): the six reads of fragments (s+1,0) and the other two loads.
+  // Stage s (buffer st = s & 1): the loads of stage s+1 go into the other
+  // buffer, which every wave finished reading before the last barrier; they
+  // are issued during the first two k-substeps (one per MFMA pair). Each
+  // k-substep's MFMAs run while the next substep's fragments are read. In the
+  // last substep, after its first MFMA pair, the wave waits for its loads of
+  // stage s+1 (issued two substeps earlier; only vmcnt(0) orders direct-to-LDS
+  // loads reliably) and meets the others at the barrier; the reads of
+  // (s+1, 0) then go with the remaining MFMA pairs.
   int st = 0;
   for (int s = 0; s < KT; ++s) {
-    const int stn = st + 1 == NS ? 0 : st + 1;
-    const int stl = st == 0 ? NS - 1 : st - 1;
-    const bool load = s + NS - 1 < KT;
-    const uint32_t kl = (uint32_t)(s + NS - 1) * BK * 2u;
-    MOE_LGKM_WAIT_TIE(fa, fb);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (load && (k & 1) == 0) MOE_BIG_DMA(stl, kl, k >> 1)
-      MOE_BIG_READ1(ga, gb, st, 1, k)
-      if (k < 2) MOE_BIG_READ1(ga, gb, st, 1, 4 + k)
-      MOE_BIG_MFMA2(fa, fb, k)
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    const int stn = st ^ 1;
+    const bool load = s + 1 < KT;
+    const uint32_t kl = (uint32_t)(s + 1) * BK * 2u;
+    MOE_BIG_SUBSTEP(fa, fb, ga, gb, st, 1, true, load, 0)
+    MOE_BIG_SUBSTEP(ga, gb, fa, fb, st, 2, true, load, 4)
+    MOE_BIG_SUBSTEP(fa, fb, ga, gb, st, 3, true, false, 0)
     MOE_LGKM_WAIT_TIE(ga, gb);
-    const bool next = s + 1 < KT;
-    if (next) {
-      // loads still allowed in flight: full stages after s+1, plus the two
-      // loads of stage s+NS-1 issued above
-      const int full = max(0, min(s + NS - 2, KT - 1) - (s + 1));
-      if (load) wait_vmcnt<4 * (NS - 3) + 2>();
-      else if (full >= 2) wait_vmcnt<8>();
-      else if (full == 1) wait_vmcnt<4>();
-      else wait_vmcnt<0>();
-      stage_barrier();
-    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      if (load && (k & 1) == 0) MOE_BIG_DMA(stl, kl, 2 + (k >> 1))
-      if (next) {
-        MOE_BIG_READ1(fa, fb, stn, 0, k)
-        if (k < 2) MOE_BIG_READ1(fa, fb, stn, 0, 4 + k)
+      if (load && k >= 1) {
+        MOE_BIG_READ1(fa, fb, stn, 0, 2 * (k - 1))
+        MOE_BIG_READ1(fa, fb, stn, 0, 2 * (k - 1) + 1)
       }
       MOE_BIG_MFMA2(ga, gb, k)
       __builtin_amdgcn_sched_barrier(0);
+      if (load && k == 0) {
+        wait_vmcnt<0>();
+        stage_barrier();
+      }
     }
     st = stn;
   }
@@ -278,17 +272,21 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
 #undef MOE_DSR
 #undef MOE_BIG_READ1
 #undef MOE_BIG_MFMA2
+#undef MOE_BIG_SUBSTEP
+  // every wave has finished its LDS reads: the stage buffers are free for the
+  // epilogue's staging
+  wait_vmcnt<0>();
+  stage_barrier();
 
   // ---- epilogue. 32x32 result layout: lane holds column (lane & 31) and, in
   // register r, row 8 (r / 4) + 4 (lane / 32) + (r % 4).
   if (!active) return;
-  // Results go through LDS so that every lane stores 16 contiguous bytes.
-  // Waves 2b, 2b+1 stage in halves of one stage buffer, none of them the last
-  // stage's (other waves may still read that one); all other buffers were
-  // retired by the last barrier, so no barrier is needed here. 128 rows x 32
-  // columns per pass, rows padded to 40 elements against bank conflicts.
+  // Results go through LDS so that every lane stores 16 contiguous bytes;
+  // each wave stages in its own 16 KB of the (now free) stage buffers.
+  // 128 rows x 32 columns per pass, rows padded to 40 elements against bank
+  // conflicts.
   constexpr int LDR = 40;
-  uint16_t* sc = (uint16_t*)&smem[((KT + (wave >> 1)) % NS) * 2 * STAGE_U4 + (wave & 1) * STAGE_U4];
+  uint16_t* sc = (uint16_t*)&smem[wave * 1024];
   const int wrows = min(128, rows - wm * 128);
   const int wrow0 = row0 + wm * 128;
   const int cc = lane & 3;          // 16-byte chunk of a staged 64-byte row

@@ -10,6 +10,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/moe_experts.h"
@@ -150,6 +151,17 @@ int launch_align(const int32_t* ids, const float* w, int M, int E, int BM, const
   return launch_status();
 }
 
+// Tuning override for the prefill GEMM's tile-group width (column tiles per
+// group); read once. MOE_EXPERTS_GROUP_COLS=<n>, n >= 1; unset = built-in choice.
+int group_cols_override() {
+  static const int v = [] {
+    const char* e = std::getenv("MOE_EXPERTS_GROUP_COLS");
+    const int n = e ? std::atoi(e) : 0;
+    return n > 0 ? n : 0;
+  }();
+  return v;
+}
+
 bool g_attr_done = false;
 int set_attrs() {
   if (g_attr_done) return MOE_OK;
@@ -225,7 +237,7 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     q.C = (uint16_t*)io.C;
     q.row_w = io.row_w;
     q.act = act_params(p);
-    q.gn = std::min(q.n_tiles, 2);
+    q.gn = std::min(q.n_tiles, group_cols_override() ? group_cols_override() : 2);
     q.xcd_remap = 1;
     const long long groups = ceil_div(q.n_tiles, q.gn);
     long long nblk = groups * pl.mt_cap * q.gn;

@@ -66,6 +66,8 @@ int check_problem(const moe_problem* p, bool grouped) {
     if (!(p->limit > 0.f)) return MOE_ENOTSUP;
   }
   if (p->H % 64 || p->I % 64) return MOE_ENOTSUP;
+  if (p->wfmt == MOE_W_MXFP4 && (p->H > moe::skinny::kMaxMxfp4K || p->I > moe::skinny::kMaxMxfp4K))
+    return MOE_ENOTSUP;
   if (p->E > kMaxExperts) return MOE_ENOTSUP;
   const long long rows = grouped ? (long long)p->T : (long long)p->T * p->k;
   if (rows > (1LL << 30)) return MOE_ENOTSUP;
@@ -169,6 +171,19 @@ int set_attrs() {
   e = hipFuncSetAttribute((const void*)moe::k_align_count, hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
   if (e == hipSuccess)
     e = hipFuncSetAttribute((const void*)moe::k_align_scatter, hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
+  // MXFP4 decode GEMM: scale rows staged in dynamic LDS, up to 4 * kMaxMxfp4K bytes
+  const void* mx[] = {
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, true, 4>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, true, 8>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, true, 16>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 4>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 8>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 16>,
+  };
+  for (const void* f : mx)
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              moe::skinny::scale_lds_bytes(moe::skinny::kMaxMxfp4K));
   if (e != hipSuccess) return MOE_EHIP;
   g_attr_done = true;
   return MOE_OK;
@@ -210,15 +225,25 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     q.seg_end = cu;
     q.status = status;
     q.mt_cap = pl.mt_cap;
-    q.n_tiles = ceil_div(io.N, moe::skinny::NW * moe::skinny::WN);
+    q.n_tiles = ceil_div(io.N, moe::skinny::block_cols(GATED));
     q.C = (uint16_t*)io.C;
     q.row_w = io.row_w;
     q.act = act_params(p);
     const dim3 grid((unsigned)pl.mt_cap * q.n_tiles);
-    if (p.wfmt == MOE_W_MXFP4)
-      hipLaunchKernelGGL((moe::skinny::k_gemm<moe::skinny::W_MXFP4, GATED>), grid, dim3(moe::skinny::NT), 0, s, q);
-    else
-      hipLaunchKernelGGL((moe::skinny::k_gemm<moe::skinny::W_BF16, GATED>), grid, dim3(moe::skinny::NT), 0, s, q);
+    const dim3 block(moe::skinny::NT);
+    using moe::skinny::k_gemm;
+    using moe::skinny::W_BF16;
+    using moe::skinny::W_MXFP4;
+    if (p.wfmt == MOE_W_MXFP4) {
+      const size_t lds = moe::skinny::scale_lds_bytes(io.K);
+      switch (moe::skinny::scale_pieces_per_thread(io.K)) {
+        case 4: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 4>), grid, block, lds, s, q); break;
+        case 8: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 8>), grid, block, lds, s, q); break;
+        default: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 16>), grid, block, lds, s, q); break;
+      }
+    } else {
+      hipLaunchKernelGGL((k_gemm<W_BF16, GATED, 0>), grid, block, 0, s, q);
+    }
   } else {
     moe::big::Params q;
     q.A = (const uint16_t*)io.A;
@@ -252,6 +277,7 @@ int check_common_ptrs(const moe_problem* p, const void* x, const void* wg, const
                       const uint8_t* sg, const uint8_t* su, const uint8_t* sd, const void* out, const void* ws) {
   if (!x || !wg || !wu || !wd || !out || !ws) return MOE_EINVAL;
   if (p->wfmt == MOE_W_MXFP4 && (!sg || !su || !sd)) return MOE_EINVAL;
+  if (p->wfmt == MOE_W_MXFP4 && (!aligned16(sg) || !aligned16(su) || !aligned16(sd))) return MOE_EINVAL;
   if (!aligned16(x) || !aligned16(wg) || !aligned16(wu) || !aligned16(wd) || !aligned16(out)) return MOE_EINVAL;
   if (((uintptr_t)ws % kAlign) != 0) return MOE_EINVAL;
   return MOE_OK;

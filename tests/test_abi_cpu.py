@@ -61,6 +61,8 @@ def test_workspace_bytes_monotone_and_aligned():
     (dict(act="swiglu_oai", limit=0.0), B.MOE_ENOTSUP),
     (dict(act="swiglu_oai", limit=-1.0), B.MOE_ENOTSUP),
     (dict(act="swiglu_oai", alpha=math.nan, limit=7.0), B.MOE_EINVAL),
+    (dict(wfmt="mxfp4", H=16448), B.MOE_ENOTSUP),  # MXFP4 scale rows beyond the LDS staging limit
+    (dict(wfmt="mxfp4", I=16448), B.MOE_ENOTSUP),
 ])
 def test_invalid_problems_rejected(kw, code):
     base = dict(T=16, H=128, I=256, E=8, k=2)
@@ -98,6 +100,13 @@ def test_bad_enum_and_pointers_rejected():
     p = B.problem(16, 128, 256, 8, 2, wfmt="mxfp4")
     assert L.moe_experts_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None, None, fake, fake,
                                  1 << 40, None) == B.MOE_EINVAL
+    # MXFP4 scale arrays must be 16-byte aligned (the decode GEMM copies them in 16-byte pieces)
+    odd_s = ctypes.c_void_p((1 << 20) + 4)
+    for i in range(3):
+        sc = [fake, fake, fake]
+        sc[i] = odd_s
+        assert L.moe_experts_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, *sc, fake, fake,
+                                     1 << 40, None) == B.MOE_EINVAL
     # timed variant: event count must be 0 or 5
     p = B.problem(16, 128, 256, 8, 2)
     ev = (ctypes.c_void_p * 3)()

@@ -85,17 +85,18 @@ def make_inputs(wl, dev):
     return x, torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev), W, S, ids, w
 
 
-def kernel_source_hash() -> str:
-    """sha256 of the sources the prefill and decode GEMMs are built from."""
+def kernel_source_hash(wfmt: str) -> str:
+    """sha256 of the sources the GEMM1 kernel of a weight format is built from
+    (bf16: the prefill GEMM; mxfp4: the decode GEMM)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("common.hpp", "gemm_bf16.hpp", "gemm_skinny.hpp"):
+    for f in ("common.hpp", "gemm_bf16.hpp" if wfmt == "bf16" else "gemm_skinny.hpp"):
         with open(os.path.join(ROOT, "mixture_experts_expert_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def counter_traffic(workload: str):
+def counter_traffic(workload: str, wfmt: str):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary
     of this workload: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled
     by what the same counter read for a 1 GiB device copy. None when there is
@@ -109,7 +110,7 @@ def counter_traffic(workload: str):
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("kernel_source_sha256") != kernel_source_hash(wfmt):
         return None
     copy_bytes = float(kv["copy_bytes"])
     f_scale = copy_bytes / (float(kv["copy_fetch_kib"]) * 1024.0)
@@ -166,7 +167,8 @@ def cpu_baseline(wl, x, ids, w, W, S, n_tokens):
 def main():
     args = parse()
     if args.print_source_hash:
-        print(kernel_source_hash())
+        import synth
+        print(kernel_source_hash(synth.WORKLOADS[args.workload].wfmt))
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the experts step "
@@ -232,7 +234,7 @@ def main():
         g1_flops = 4.0 * M * wl.H * wl.I
         achieved = g1_flops / (avg["gemm1"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": counter_traffic(wl.name),
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": counter_traffic(wl.name, wl.wfmt),
                 "kernel": "gemm1 (gate+up, bf16)",
                 "algorithmic_bytes": n_touched * 2 * wl.I * wl.H * 2 + M * wl.H * 2 + M * wl.I * 2}
     else:
@@ -242,7 +244,7 @@ def main():
         g1_bytes = n_touched * 2 * wl.H * wl.I * (0.5 + 1 / 32)
         achieved = g1_bytes / (avg["gemm1"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic(wl.name),
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic(wl.name, wl.wfmt),
                 "kernel": "gemm1 (gate+up, MXFP4)", "algorithmic_bytes": g1_bytes}
 
     res = {

@@ -217,7 +217,10 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   {                                                                              \
     MOE_LGKM_WAIT_TIE(cA, cB);                                                   \
     _Pragma("unroll") for (int k = 0; k < 4; ++k) {                              \
-      if (dma) MOE_BIG_DMA(stn, kl, (q0) + k)                                   \
+      if (dma) {                                                                 \
+        MOE_BIG_DMA(stn, kl, 2 * k)                                              \
+        MOE_BIG_DMA(stn, kl, 2 * k + 1)                                          \
+      }                                                                          \
       if (rd) {                                                                  \
         MOE_BIG_READ1(nA, nB, nst, nks, k)                                       \
         if (k < 2) MOE_BIG_READ1(nA, nB, nst, nks, 4 + k)                        \
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
     const bool load = s + 1 < KT;
     const uint32_t kl = (uint32_t)(s + 1) * BK * 2u;
     MOE_BIG_SUBSTEP(fa, fb, ga, gb, st, 1, true, load, 0)
-    MOE_BIG_SUBSTEP(ga, gb, fa, fb, st, 2, true, load, 4)
+    MOE_BIG_SUBSTEP(ga, gb, fa, fb, st, 2, true, false, 0)
     MOE_BIG_SUBSTEP(fa, fb, ga, gb, st, 3, true, false, 0)
     MOE_LGKM_WAIT_TIE(ga, gb);
 #pragma unroll

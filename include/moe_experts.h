@@ -98,7 +98,10 @@ typedef struct {
   size_t inv_perm;   /* int32[T*k] flat slot -> sorted row, -1 for masked / bad ids */
   size_t w_sorted;   /* float[T*k] route weight per sorted row */
   size_t act;        /* bf16 [T*k, I] activation rows in sorted order */
-  size_t y;          /* bf16 [T*k, H] down-projection rows in sorted order */
+  size_t y;          /* bf16 [S, T*k, H] down-projection rows in sorted order; when the
+                        down projection's K is split into S ranges (S <= 4, chosen on
+                        the device to fill the compute units; 1 on the decode path),
+                        partial sums per range, added by the combine */
   size_t total;      /* = moe_experts_workspace_bytes() */
 } moe_ws_layout;
 

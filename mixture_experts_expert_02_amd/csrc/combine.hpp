@@ -11,22 +11,37 @@
 
 namespace moe {
 
-// One workgroup per token; each thread sums 8 consecutive columns.
+// The down projection may come in S partial outputs over K ranges (S from
+// split_k_count with the GEMM's own arguments; 1 when s_cap is 1).
+struct SplitSum {
+  const int32_t* status;  // status[2] = row tiles of the GEMM
+  int32_t n_tiles;        // GEMM2 column tiles
+  int32_t kt;             // GEMM2 K stages
+  int32_t ncu;
+  int32_t s_cap;
+  int64_t stride;         // elements between partial outputs
+};
+
+// One workgroup per token; each thread sums 8 consecutive columns, slot j
+// outer and K range s inner, both ascending.
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* y, const int32_t* inv_perm, int T, int k,
-                                                 int H, uint16_t* out) {
+                                                 int H, const SplitSum ss, uint16_t* out) {
   const int t = blockIdx.x;
   if (t >= T) return;
+  const int S = ss.s_cap > 1 ? split_k_count(ss.status[2] * ss.n_tiles, ss.kt, ss.ncu, ss.s_cap) : 1;
   for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
       const int p = inv_perm[(size_t)t * k + j];
       if (p < 0) continue;
-      const u32x4 v = *(const u32x4*)(y + (size_t)p * H + h);
-      const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+      for (int sp = 0; sp < S; ++sp) {
+        const u32x4 v = *(const u32x4*)(y + (size_t)sp * ss.stride + (size_t)p * H + h);
+        const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += bf16_bits_to_f32(w[i] & 0xffffu);
-        acc[2 * i + 1] += bf16_bits_to_f32(w[i] >> 16);
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += bf16_bits_to_f32(w[i] & 0xffffu);
+          acc[2 * i + 1] += bf16_bits_to_f32(w[i] >> 16);
+        }
       }
     }
     u32x4 o;

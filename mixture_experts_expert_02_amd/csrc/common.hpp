@@ -70,6 +70,26 @@ __device__ __forceinline__ uint64_t match_key(int key, int nbits) {
   return m;
 }
 
+// Split of the down projection's K range (GEMM2 of the big-tile path): the
+// number of K ranges S (1..s_cap) that minimises rounds x stages per block,
+// where a round is one tile per compute unit and each block carries about
+// two stages of fixed cost (first loads, epilogue). Pure function of its
+// arguments: the GEMM and the combine that sums the S partial outputs both
+// call it and get the same S.
+__host__ __device__ inline int split_k_count(int tiles, int kt, int ncu, int s_cap) {
+  int best = 1;
+  long long best_cost = -1;
+  for (int s = 1; s <= s_cap && s <= kt; ++s) {
+    const long long rounds = ((long long)tiles * s + ncu - 1) / ncu;
+    const long long cost = rounds * ((kt + s - 1) / s + 2);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
+}
+
 // Hardware dispatches workgroup b to XCD (b mod 8). Renumber so that
 // consecutive logical ids run on the same XCD and share its L2.
 // nblk must be a multiple of 8.

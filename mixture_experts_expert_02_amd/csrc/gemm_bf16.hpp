@@ -54,7 +54,10 @@ struct Params {
   int32_t n_tiles;         // column tiles
   int32_t gn;              // column tiles per tile group
   int32_t xcd_remap;       // 1: renumber workgroups so consecutive tiles share an XCD
-  uint16_t* C;             // [rows, N] bf16 output, sorted row order
+  int32_t s_cap;           // GEMM2: at most this many K ranges per tile (1 = no split)
+  int32_t ncu;             // compute units of the device (one block each)
+  int64_t c_split;         // elements between the partial outputs of consecutive K ranges
+  uint16_t* C;             // [rows, N] bf16 output, sorted row order (GEMM2 split: [S, rows, N])
   const float* row_w;      // GEMM1: route weight per sorted row
   ActParams act;
 };
@@ -107,10 +110,21 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA targets go in M0
 
-  // block -> (row tile, column tile): groups of gn column tiles, row tiles
-  // inside a group, column tile fastest; optionally logical ids contiguous
-  // per XCD so that tiles sharing weight and row panels share an L2
-  const int L = p.xcd_remap ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  // block -> (row tile, column tile[, K range]): groups of gn column tiles,
+  // row tiles inside a group, column tile fastest; optionally logical ids
+  // contiguous per XCD so that tiles sharing weight and row panels share an
+  // L2. GEMM2 may split K into S ranges (split_k_count) when there are too
+  // few tiles to fill the last round: the K range is the fastest index, so
+  // that the blocks of unused ranges (S < s_cap) spread evenly over the XCDs,
+  // and each range writes its own partial output, summed by the combine.
+  const int L0 = p.xcd_remap ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  int L = L0, split = 0, nsplit = 1;
+  if (!GATED && p.s_cap > 1) {
+    split = L0 % p.s_cap;
+    L = L0 / p.s_cap;
+    nsplit = split_k_count(p.status[2] * p.n_tiles, p.K / BK, p.ncu, p.s_cap);
+    if (split >= nsplit) return;
+  }
   const int span = p.mt_cap * p.gn;
   const int grp = L / span;
   const int r_in = L - grp * span;
@@ -129,6 +143,10 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   // l%8, which holds global chunk (l%8) ^ ((row >> 1) & 7). Wave w fills
   // blocks 4w..4w+3 (rows 32w..32w+31) of the A and of the B half.
   // 32-bit byte offsets: the host keeps T*H, M*I and N*K below 2^31 elements.
+  // This block's K range: stages [st_lo, st_lo + KT) of K / BK.
+  const int st_lo = split * (K / BK) / nsplit;
+  const int KT = (split + 1) * (K / BK) / nsplit - st_lo;
+  const uint32_t kb0 = (uint32_t)st_lo * BK * 2u;
   const char* __restrict__ Ab = (const char*)p.A;
   const char* __restrict__ B0b = (const char*)(p.B0 + (size_t)seg * N * K);
   const char* __restrict__ B1b = GATED ? (const char*)(p.B1 + (size_t)seg * N * K) : B0b;
@@ -141,9 +159,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
       const int chunk = (lane & 7) ^ ((r >> 1) & 7);
       int arow = first;
       if (r < rows) arow = p.a_perm ? p.a_perm[row0 + r] / p.a_div : row0 + r;
-      a_off[i] = ((uint32_t)arow * (uint32_t)K + chunk * 8) * 2u;
+      a_off[i] = ((uint32_t)arow * (uint32_t)K + chunk * 8) * 2u + kb0;
       const int n = min(n0 + (GATED ? (r & 127) : r), N - 1);
-      b_off[i] = ((uint32_t)n * (uint32_t)K + chunk * 8) * 2u;
+      b_off[i] = ((uint32_t)n * (uint32_t)K + chunk * 8) * 2u + kb0;
     }
   }
   // In GEMM1, rows 0..127 of the B half are gate rows (waves 0-3) and rows
@@ -230,7 +248,6 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
     }                                                                            \
   }
 
-  const int KT = K / BK;
   // prologue: stage 0
 #pragma unroll
   for (int q = 0; q < 8; ++q) MOE_BIG_DMA(0, 0u, q)
@@ -291,6 +308,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   constexpr int LDR = 40;
   uint16_t* sc = (uint16_t*)&smem[wave * 1024];
   const int wrows = min(128, rows - wm * 128);
+  uint16_t* __restrict__ Cs = p.C + (size_t)split * p.c_split;
   const int wrow0 = row0 + wm * 128;
   const int cc = lane & 3;          // 16-byte chunk of a staged 64-byte row
   const int rr = lane >> 2;         // staged row within a group of 16
@@ -324,7 +342,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
       for (int t = 0; t < 8; ++t) {
         const int row = t * 16 + rr;
         if (row < wrows)
-          *(u32x4*)(p.C + (size_t)(wrow0 + row) * N + col0) = *(const u32x4*)&sc[row * LDR + cc * 8];
+          *(u32x4*)(Cs + (size_t)(wrow0 + row) * N + col0) = *(const u32x4*)&sc[row * LDR + cc * 8];
       }
     }
   }

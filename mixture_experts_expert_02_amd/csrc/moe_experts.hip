@@ -25,6 +25,7 @@ constexpr int kMaxExperts = 4096;
 constexpr int kFusedMaxRows = 4096;
 constexpr int kFusedMaxExperts = 1024;
 constexpr size_t kAlign = 256;
+constexpr int kMaxSplitK = 4;
 
 size_t up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -48,6 +49,7 @@ struct Plan {
   bool skinny;
   int BM;
   int mt_cap;
+  int s_cap;     // GEMM2 K ranges the y buffer has room for (token-major big-tile path)
   bool fused_align;
   int chunk, nch;
   // byte offsets
@@ -74,12 +76,29 @@ int check_problem(const moe_problem* p, bool grouped) {
   return MOE_OK;
 }
 
-Plan make_plan(const moe_problem& p, bool grouped) {
+// Upper bound on GEMM2's K ranges: MOE_EXPERTS_MAX_SPLIT_K=<n> (n >= 1), read
+// at every call (tests use it to pin the split); unset = kMaxSplitK.
+int max_split_k() {
+  const char* e = std::getenv("MOE_EXPERTS_MAX_SPLIT_K");
+  const int n = e ? std::atoi(e) : 0;
+  return n > 0 ? std::min(n, kMaxSplitK) : kMaxSplitK;
+}
+
+// Workspace layout of problem p. The y buffer comes last and holds s_cap
+// partial outputs; with ws_bytes given, s_cap shrinks to what fits, so a
+// workspace sized for a larger T (fewer K ranges, more rows) still serves.
+Plan make_plan(const moe_problem& p, bool grouped, size_t ws_bytes = ~(size_t)0) {
   Plan pl{};
   pl.M = grouped ? (long long)p.T : (long long)p.T * p.k;
   pl.skinny = use_skinny(p, pl.M);
   pl.BM = pl.skinny ? moe::skinny::BM : moe::big::BM;
   pl.mt_cap = ceil_div(pl.M, pl.BM) + (int)std::min<long long>(p.E, pl.M);
+  // Splitting GEMM2's K only pays when its tiles fill a few rounds of the
+  // compute units at most; with up to 1024 tiles (four rounds of 256 units)
+  // room is kept for four partial outputs.
+  pl.s_cap = 1;
+  if (!grouped && !pl.skinny && (long long)pl.mt_cap * ceil_div(p.H, moe::big::BN) <= 1024)
+    pl.s_cap = std::max(1, std::min(max_split_k(), p.I / moe::big::BK));
   pl.fused_align = !grouped && pl.M <= kFusedMaxRows && p.E <= kFusedMaxExperts;
   if (!grouped && !pl.fused_align) {
     pl.chunk = (int)std::max<long long>(512, (ceil_div(pl.M, 256) + 63) / 64 * 64);
@@ -107,7 +126,13 @@ Plan make_plan(const moe_problem& p, bool grouped) {
     pl.w_sorted = take(4ull * pl.M);
   }
   pl.act = take(2ull * pl.M * p.I);
-  if (!grouped) pl.y = take(2ull * pl.M * p.H);
+  if (!grouped) {
+    pl.y = o;
+    const size_t one = 2ull * pl.M * p.H;
+    if (pl.s_cap > 1 && ws_bytes >= pl.y + one && ws_bytes < pl.y + one * pl.s_cap)
+      pl.s_cap = (int)((ws_bytes - pl.y) / one);
+    take(one * pl.s_cap);
+  }
   pl.total = o;
   return pl;
 }
@@ -124,6 +149,22 @@ moe::ActParams act_params(const moe_problem& p) {
   a.beta = p.beta;
   a.limit = p.limit;
   return a;
+}
+
+// Compute units of the current device, cached per device.
+int device_cus(int* n) {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *n = cache[dev];
+    return MOE_OK;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return MOE_EHIP;
+  if (dev >= 0 && dev < 64) cache[dev] = v;
+  *n = v;
+  return MOE_OK;
 }
 
 int launch_status() {
@@ -201,6 +242,8 @@ struct GemmIO {
   int N, K;
   void* C;
   const float* row_w;
+  int s_cap;         // GEMM2: K ranges with room in C (1 = C is [rows, N])
+  long long c_split; // elements between partial outputs
 };
 
 template <bool GATED>
@@ -264,8 +307,12 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     q.act = act_params(p);
     q.gn = std::min(q.n_tiles, group_cols_override() ? group_cols_override() : 2);
     q.xcd_remap = 1;
+    q.s_cap = GATED ? 1 : io.s_cap;
+    q.c_split = io.c_split;
+    int rc = device_cus(&q.ncu);
+    if (rc) return rc;
     const long long groups = ceil_div(q.n_tiles, q.gn);
-    long long nblk = groups * pl.mt_cap * q.gn;
+    long long nblk = groups * pl.mt_cap * q.gn * q.s_cap;
     nblk = (nblk + 7) / 8 * 8;
     if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
     hipLaunchKernelGGL((moe::big::k_gemm<GATED>), dim3((unsigned)nblk), dim3(moe::big::NT), 0, s, q);
@@ -293,7 +340,7 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
   if (rc) return rc;
   if (n_ev != 0 && (n_ev != 5 || !ev)) return MOE_EINVAL;
   if (p->T == 0) return MOE_OK;
-  const Plan pl = make_plan(*p, false);
+  const Plan pl = make_plan(*p, false, ws_bytes);
   if (ws_bytes < pl.total) return MOE_ENOSPC;
   if ((rc = set_attrs())) return rc;
   auto mark = [&](int i) {
@@ -315,17 +362,21 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
   mark(0);
   if ((rc = launch_align(ids, tw, M, p->E, pl.BM, pl, o, ws, s))) return rc;
 
-  GemmIO g1{x, o.perm, p->k, wg, wu, sg, su, p->I, p->H, at<void>(ws, pl.act), o.w_sorted};
+  GemmIO g1{x, o.perm, p->k, wg, wu, sg, su, p->I, p->H, at<void>(ws, pl.act), o.w_sorted, 1, 0};
   mark(1);
   if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
 
-  GemmIO g2{at<void>(ws, pl.act), nullptr, 1, wd, nullptr, sd, nullptr, p->H, p->I, at<void>(ws, pl.y), nullptr};
+  const long long y_split = pl.M * p->H;
+  GemmIO g2{at<void>(ws, pl.act), nullptr, 1, wd, nullptr, sd, nullptr, p->H, p->I, at<void>(ws, pl.y), nullptr,
+            pl.s_cap, y_split};
   mark(2);
   if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
 
   mark(3);
+  moe::SplitSum ss{o.status, ceil_div(p->H, moe::big::BN), p->I / moe::big::BK, 1, pl.s_cap, y_split};
+  if (pl.s_cap > 1 && (rc = device_cus(&ss.ncu))) return rc;
   hipLaunchKernelGGL(moe::k_combine, dim3(p->T), dim3(256), 0, s, at<const uint16_t>(ws, pl.y),
-                     (const int32_t*)o.inv_perm, p->T, p->k, p->H, (uint16_t*)out);
+                     (const int32_t*)o.inv_perm, p->T, p->k, p->H, ss, (uint16_t*)out);
   mark(4);
   return launch_status();
 }
@@ -442,9 +493,9 @@ int moe_experts_forward_grouped(const moe_problem* p, const void* x_nvs, const i
   hipLaunchKernelGGL(moe::k_grouped_prep, dim3(1), dim3(1024), (size_t)(3 * p->E + 32) * 4, s, cu_seqlens, p->E,
                      p->T, pl.BM, o);
   if ((rc = launch_status())) return rc;
-  GemmIO g1{x_nvs, nullptr, 1, w_gate, w_up, s_gate, s_up, p->I, p->H, at<void>(ws, pl.act), route_w};
+  GemmIO g1{x_nvs, nullptr, 1, w_gate, w_up, s_gate, s_up, p->I, p->H, at<void>(ws, pl.act), route_w, 1, 0};
   if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
-  GemmIO g2{at<void>(ws, pl.act), nullptr, 1, w_down, nullptr, s_down, nullptr, p->H, p->I, out_nvs, nullptr};
+  GemmIO g2{at<void>(ws, pl.act), nullptr, 1, w_down, nullptr, s_down, nullptr, p->H, p->I, out_nvs, nullptr, 1, 0};
   if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
   hipLaunchKernelGGL(moe::k_zero_tail, dim3(p->T), dim3(256), 0, s, (uint16_t*)out_nvs,
                      (const int32_t*)o.status, p->T, p->H);

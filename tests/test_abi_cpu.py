@@ -50,6 +50,23 @@ def test_workspace_bytes_monotone_and_aligned():
     assert lay.act % 256 == 0 and lay.y % 256 == 0 and lay.y >= lay.act + 8192 * 14336 * 2
 
 
+def test_workspace_room_for_split_down_projection(monkeypatch):
+    # Few tiles (Mixtral-shaped prefill): y holds up to four partial outputs of
+    # the down projection; MOE_EXPERTS_MAX_SPLIT_K caps that. Many tiles
+    # (256 experts): no split, one output.
+    p = B.problem(4096, 4096, 14336, 8, 2)
+    full = B.moe_experts_workspace_bytes(p)
+    monkeypatch.setenv("MOE_EXPERTS_MAX_SPLIT_K", "1")
+    one = B.moe_experts_workspace_bytes(p)
+    assert full - one == 3 * 8192 * 4096 * 2
+    lay = B.moe_experts_workspace_layout(p)
+    assert lay.total == lay.y + 8192 * 4096 * 2
+    monkeypatch.delenv("MOE_EXPERTS_MAX_SPLIT_K")
+    q = B.problem(8192, 7168, 2048, 256, 8)
+    lay = B.moe_experts_workspace_layout(q)
+    assert lay.total == lay.y + 65536 * 7168 * 2
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(H=100), B.MOE_ENOTSUP),                 # not a multiple of 64
     (dict(I=96), B.MOE_ENOTSUP),

@@ -123,6 +123,24 @@ def test_tiny_workload_and_intermediates():
     assert rel_err(to_np(act), a_ref) <= TOL
 
 
+@pytest.mark.parametrize("max_split", [1, 2, 3, 4])
+def test_split_down_projection_matches_oracle(max_split, monkeypatch):
+    # A problem with few tiles splits the down projection's K (6 stages of 64)
+    # into as many ranges as allowed: 1, 2, 3 (2+2+2) or 4 (1+1+2+2 stages);
+    # the combine adds the partial outputs.
+    monkeypatch.setenv("MOE_EXPERTS_MAX_SPLIT_K", str(max_split))
+    T, H, I, E, k = 700, 320, 384, 5, 2
+    print(f"[forward] split<={max_split} T={T} H={H} I={I} E={E} k={k}", flush=True)
+    x, ids, w, W, S = make_problem(11, T, H, I, E, k, "bf16")
+    out = run_gpu(x, ids, w, W, S, dict(act="silu"))
+    ref = oracle_out(x, ids, w, W, S, dict(act="silu"))
+    err = rel_err(to_np(out), ref)
+    print(f"[forward] split<={max_split} rel err {err:.2e}", flush=True)
+    assert err <= TOL
+    again = run_gpu(x, ids, w, W, S, dict(act="silu"))
+    assert torch.equal(out, again)
+
+
 @pytest.mark.parametrize("shape,wfmt", [((700, 256, 384, 5, 2), "bf16"), ((9, 256, 320, 6, 3), "mxfp4")])
 def test_forward_is_bitwise_deterministic(shape, wfmt):
     T, H, I, E, k = shape

@@ -72,16 +72,17 @@ __device__ __forceinline__ uint64_t match_key(int key, int nbits) {
 
 // Split of the down projection's K range (GEMM2 of the big-tile path): the
 // number of K ranges S (1..s_cap) that minimises rounds x stages per block,
-// where a round is one tile per compute unit and each block carries about
-// two stages of fixed cost (first loads, epilogue). Pure function of its
-// arguments: the GEMM and the combine that sums the S partial outputs both
-// call it and get the same S.
+// where a round is one tile per compute unit and each block carries a fixed
+// cost worth about 12 stages (first loads, epilogue, and the partial output
+// written and read back by the combine; fitted to Mixtral-shaped timings,
+// where 3 ranges beat 4). Pure function of its arguments: the GEMM and the
+// combine that sums the S partial outputs both call it and get the same S.
 __host__ __device__ inline int split_k_count(int tiles, int kt, int ncu, int s_cap) {
   int best = 1;
   long long best_cost = -1;
   for (int s = 1; s <= s_cap && s <= kt; ++s) {
     const long long rounds = ((long long)tiles * s + ncu - 1) / ncu;
-    const long long cost = rounds * ((kt + s - 1) / s + 2);
+    const long long cost = rounds * ((kt + s - 1) / s + 12);
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
       best = s;
@@ -90,11 +91,5 @@ __host__ __device__ inline int split_k_count(int tiles, int kt, int ncu, int s_c
   return best;
 }
 
-// Hardware dispatches workgroup b to XCD (b mod 8). Renumber so that
-// consecutive logical ids run on the same XCD and share its L2.
-// nblk must be a multiple of 8.
-__device__ __forceinline__ int xcd_logical_block(int b, int nblk) {
-  return (b & 7) * (nblk >> 3) + (b >> 3);
-}
 
 }  // namespace moe

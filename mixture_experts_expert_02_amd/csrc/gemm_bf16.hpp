@@ -110,27 +110,46 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA targets go in M0
 
-  // block -> (row tile, column tile[, K range]): groups of gn column tiles,
-  // row tiles inside a group, column tile fastest; optionally logical ids
-  // contiguous per XCD so that tiles sharing weight and row panels share an
-  // L2. GEMM2 may split K into S ranges (split_k_count) when there are too
-  // few tiles to fill the last round: the K range is the fastest index, so
-  // that the blocks of unused ranges (S < s_cap) spread evenly over the XCDs,
-  // and each range writes its own partial output, summed by the combine.
-  const int L0 = p.xcd_remap ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
-  int L = L0, split = 0, nsplit = 1;
-  if (!GATED && p.s_cap > 1) {
-    split = L0 % p.s_cap;
-    L = L0 / p.s_cap;
-    nsplit = split_k_count(p.status[2] * p.n_tiles, p.K / BK, p.ncu, p.s_cap);
-    if (split >= nsplit) return;
+  // block -> work item -> (row tile, column tile[, K range]). Only the
+  // device knows the number of row tiles, so the grid covers an upper bound
+  // and the items are numbered compactly over the live ones: blocks past the
+  // last item exit, and they are the last blocks dispatched (blocks that exit
+  // at once, interleaved with live ones, have left whole shader engines idle).
+  // With xcd_remap (the hardware sends workgroup b to XCD b mod 8), each XCD
+  // takes a contiguous run of items, so tiles that share weight and row
+  // panels share an L2. Items: groups of gn column
+  // tiles, row tiles inside a group, column tile fastest. GEMM2 may split K
+  // into S ranges (split_k_count) when there are too few tiles to fill the
+  // last round; the K range is the fastest index, and each range writes its
+  // own partial output, summed by the combine.
+  const int mtl = p.status[2];
+  int nsplit = 1;
+  if (!GATED && p.s_cap > 1) nsplit = split_k_count(mtl * p.n_tiles, p.K / BK, p.ncu, p.s_cap);
+  const int n_live = mtl * p.n_tiles * nsplit;
+  int item = blockIdx.x;
+  if (p.xcd_remap) {
+    const int per = (n_live + 7) >> 3;
+    const int j = blockIdx.x >> 3;
+    if (j >= per) return;
+    item = (blockIdx.x & 7) * per + j;
   }
-  const int span = p.mt_cap * p.gn;
-  const int grp = L / span;
-  const int r_in = L - grp * span;
-  const int mt = r_in / p.gn;
-  const int nt = grp * p.gn + (r_in - mt * p.gn);
-  if (nt >= p.n_tiles || mt >= p.status[2]) return;
+  if (item >= n_live) return;
+  const int split = item % nsplit;
+  const int tl = item / nsplit;
+  const int full = p.n_tiles / p.gn;  // groups of exactly gn column tiles
+  int mt, nt;
+  if (tl < full * mtl * p.gn) {
+    const int span = mtl * p.gn;
+    const int grp = tl / span;
+    const int r_in = tl - grp * span;
+    mt = r_in / p.gn;
+    nt = grp * p.gn + (r_in - mt * p.gn);
+  } else {  // the last, narrower group
+    const int gl = p.n_tiles - full * p.gn;
+    const int r_in = tl - full * mtl * p.gn;
+    mt = r_in / gl;
+    nt = full * p.gn + (r_in - mt * gl);
+  }
 
   const int seg = p.tile_seg[mt];
   const int row0 = p.tile_row0[mt];

@@ -311,8 +311,7 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     q.c_split = io.c_split;
     int rc = device_cus(&q.ncu);
     if (rc) return rc;
-    const long long groups = ceil_div(q.n_tiles, q.gn);
-    long long nblk = groups * pl.mt_cap * q.gn * q.s_cap;
+    long long nblk = (long long)pl.mt_cap * q.n_tiles * q.s_cap;
     nblk = (nblk + 7) / 8 * 8;
     if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
     hipLaunchKernelGGL((moe::big::k_gemm<GATED>), dim3((unsigned)nblk), dim3(moe::big::NT), 0, s, q);

@@ -7,20 +7,28 @@
 // docstring). Weights may be bf16 or MXFP4 (trtllm_mxfp4_moe page,
 // TrtLlmMxfp4ExpertsBase._supports_quant_scheme: MXFP4 weights with
 // unquantized activations): e2m1 codes with an e8m0 scale per 32 K elements
-// (OCP Microscaling v1.0 reading). MXFP4 codes are decoded to bf16 in
-// registers with v_cvt_scalef32_pk_bf16_fp4; every e2m1 value times a power of
-// two in the bf16 range is exact in bf16, so the MFMA sees the exact weights.
+// (OCP Microscaling v1.0 reading).
 //
 // Tile: 16 rows. Each wave owns two 16-column weight streams: gate and up of
 // the same 16 columns (GEMM1), or two adjacent 16-column groups (GEMM2), so a
 // wave moves the same bytes per K step in both GEMMs. 4 waves per workgroup.
-// v_mfma_f32_16x16x32_bf16 with the activations as the A operand (row =
-// lane & 15) and the weights as the B operand (column = lane & 15). The K
-// order inside a dot product is free as long as A and B agree, so in K step s
-// (128 values) lane group q = lane >> 4 owns the 32-value scale block
-// kb = 4 s + q: one 16-byte load carries a lane's 32 MXFP4 codes, whose single
-// scale comes with them, and feeds four MFMAs of 8 K values each; the 16 lanes
-// of a group read 64 contiguous bytes of each of 16 weight rows.
+// The activations are the MFMA's A operand (row = lane & 15), the weights its
+// B operand (column = lane & 15). In K step s (128 values) lane group
+// q = lane >> 4 owns the 32-value scale block kb = 4 s + q of the weights: one
+// 16-byte load carries a lane's 32 MXFP4 codes, whose single scale comes with
+// them; the 16 lanes of a group read 64 contiguous bytes of each of 16 rows.
+//
+// bf16 weights: four v_mfma_f32_16x16x32_bf16 per step and stream (the K
+// order inside a dot product is free as long as A and B agree).
+// MXFP4 weights: the codes go to v_mfma_scale_f32_16x16x128_f8f6f4 as they
+// are, with their e8m0 scales, so nothing is decoded. Its A operand is e4m3
+// with a scale per 32 K values: the activation rows are split beforehand
+// (k_quant_rows) into two e4m3 parts per value, hi + lo, which together
+// carry every bit of the bf16 value (to within 2^-17 of the block's largest
+// value), and the step runs one MFMA per part. Lane group q then holds
+// activation K values 16 q..16 q+15 and 64 + 16 q..64 + 16 q + 15 of the step
+// (the operand layout of the fp8 A input), and supplies the scales of block q
+// for both operands.
 //
 // MXFP4 scales: the e8m0 bytes of a workgroup's weight rows form one
 // contiguous region per stream (64 rows x K/32 bytes for gate and for up, or
@@ -57,8 +65,28 @@ constexpr int kMaxMxfp4K = 16384;
 __host__ __device__ constexpr int scale_lds_bytes(int K) { return 4 * K; }
 __host__ __device__ constexpr int scale_pieces_per_thread(int K) { return K <= 4096 ? 4 : K <= 8192 ? 8 : 16; }
 
+// Activation rows split for the block-scaled MFMA (MXFP4 weights). Each
+// 32-value block of a bf16 row gets the scale 2^s with s = e - 7, where
+// 2^e <= the block's largest magnitude < 2^(e+1), so every scaled value v lies
+// below 256 in magnitude (e4m3 reaches 448); v is written as two e4m3 values
+// hi = rne(v) and lo = rne(v - hi). A bf16 has 8 significant bits and hi
+// keeps the top 4, so v - hi needs at most 4 and hi + lo = v exactly while lo
+// stays a normal e4m3 (|v| >= 2); below that lo is off by at most half the
+// subnormal spacing 2^-9, i.e. 2^-17 of the block's largest value.
+// Layout: hi [rows, K] bytes, lo [rows, K] bytes, e8m0 codes s + 127 in rows
+// of sc_stride bytes (a multiple of 16 >= K / 32; code 0 past K / 32).
+struct QRows {
+  uint8_t* hi;
+  uint8_t* lo;
+  uint8_t* sc;
+  int32_t sc_stride;
+};
+
+__host__ __device__ constexpr int quant_sc_stride(int K) { return (K / 32 + 15) / 16 * 16; }
+
 struct Params {
-  const uint16_t* A;      // rows [*, K] bf16
+  const uint16_t* A;      // rows [*, K] bf16 (bf16 weights)
+  QRows Aq;               // the same rows split by k_quant_rows (MXFP4 weights)
   const int32_t* a_perm;  // sorted row -> flat slot, or nullptr
   int32_t a_div;
   const void* B0;         // gate / down: bf16 [G, N, K] or e2m1 codes [G, N, K/2]
@@ -77,33 +105,65 @@ struct Params {
   ActParams act;
 };
 
-// e8m0 scale code -> f32 2^(v - 127); 0 -> 2^-127 (subnormal), 255 -> NaN.
-// Written as selects so that it stays branch-free.
-__device__ __forceinline__ float e8m0_to_f32(uint32_t v) {
-  const uint32_t bits = v == 0u ? 0x00400000u : v == 255u ? 0x7fc00000u : v << 23;
-  return __uint_as_float(bits);
-}
-
-// 8 e2m1 codes (one dword, element 2i in the low nibble of byte i) -> 8 bf16
-__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float scale) {
-  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
-  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
-  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
-  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
-  bf16x8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
+// One workgroup per row, one 32-value block per thread.
+__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ src, int rows, int K, QRows q) {
+  const int r = blockIdx.x;
+  if (r >= rows) return;
+  const int KB = K / 32;
+  for (int b = threadIdx.x; b < q.sc_stride; b += 256) {
+    if (b >= KB) {
+      q.sc[(size_t)r * q.sc_stride + b] = 0;
+      continue;
+    }
+    const u32x4* in = (const u32x4*)(src + (size_t)r * K + 32 * b);
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 v = in[i];
+      w[4 * i] = v[0]; w[4 * i + 1] = v[1]; w[4 * i + 2] = v[2]; w[4 * i + 3] = v[3];
+    }
+    uint32_t mx = 0;  // largest magnitude, as bf16 bits
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = max(mx, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+    const int code = min(max((int)((mx >> 7) & 0xffu) - 7, 0), 254);
+    const float inv = __uint_as_float((uint32_t)(254 - code) << 23);  // 2^(127 - code), normal for code <= 247
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v0 = bf16_bits_to_f32(w[2 * i] & 0xffffu) * inv, v1 = bf16_bits_to_f32(w[2 * i] >> 16) * inv;
+      const float v2 = bf16_bits_to_f32(w[2 * i + 1] & 0xffffu) * inv, v3 = bf16_bits_to_f32(w[2 * i + 1] >> 16) * inv;
+      int h = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+      h = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, h, true);
+      const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false), h23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+      int l = __builtin_amdgcn_cvt_pk_fp8_f32(v0 - h01[0], v1 - h01[1], 0, false);
+      l = __builtin_amdgcn_cvt_pk_fp8_f32(v2 - h23[0], v3 - h23[1], l, true);
+      hi[i] = (uint32_t)h;
+      lo[i] = (uint32_t)l;
+    }
+    u32x4* ho = (u32x4*)(q.hi + (size_t)r * K + 32 * b);
+    u32x4* lw = (u32x4*)(q.lo + (size_t)r * K + 32 * b);
+    ho[0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    ho[1] = u32x4{hi[4], hi[5], hi[6], hi[7]};
+    lw[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    lw[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
+    q.sc[(size_t)r * q.sc_stride + b] = (uint8_t)code;
+  }
 }
 
 template <int FMT>
 struct Cfg {
   static constexpr int SPC = FMT == W_MXFP4 ? 4 : 1;  // K steps per chunk
   static constexpr int KC = SPC * 128;                // K values per chunk
-  static constexpr int LROW = KC + 8;                 // LDS row stride (bf16): 16 B pad
+  // bf16 activations: rows of KC + 8 values (16 B pad)
+  static constexpr int LROW = KC + 8;
   static constexpr int PIECES = BM * KC / 8;          // 16-byte pieces of an A chunk
   static constexpr int PPT = PIECES / NT;             // pieces per thread
   static_assert(PIECES % NT == 0, "A chunk must split evenly over the workgroup");
+  // split activations: hi and lo rows of KC + 16 bytes, then 16 rows of the
+  // chunk's KC / 32 scale bytes (16 B)
+  static constexpr int QROW = KC + 16;
+  static constexpr int QPPT = BM * KC / 16 / NT;      // 16-byte pieces of hi (and of lo) per thread
+  static constexpr int BUF_BYTES = FMT == W_MXFP4 ? 2 * BM * QROW + BM * 16 : BM * LROW * 2;
 };
 
 // The weights of one lane for one K step: 32 consecutive K values of row n.
@@ -118,35 +178,29 @@ struct WSet {
   WChunk<FMT> w0[Cfg<FMT>::SPC], w1[Cfg<FMT>::SPC];
 };
 
-// Raw loads of one lane's K block (no selects here: a value consumed right
-// after its load would make the compiler wait for it early). The block index
-// is clamped to the row, so every lane issues the same loads; compute()
-// neutralises blocks past the row end.
-template <int FMT>
-__device__ __forceinline__ void load_w(WChunk<FMT>& w, const void* Bm, size_t row, int K, int kb) {
-  const int kbc = min(kb, K / 32 - 1);
-  if (FMT == W_BF16) {
-    const u32x4* src = (const u32x4*)((const uint16_t*)Bm + row * K + (size_t)kbc * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w.q[i] = src[i];
-  } else {
-    w.q[0] = *(const u32x4*)((const uint8_t*)Bm + row * (K / 2) + (size_t)kbc * 16);
-  }
+// Weight loads go through a buffer resource over one segment's weight rows:
+// a lane's block offset needs no clamping, since a block past a row's end
+// reads the next row (finite codes that meet zero activations) or, past the
+// segment's last row, reads 0; the per-step offsets become immediates.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// MFMA B operand i (8 K values) of a lane's block. A block past the row end
-// (!ok) multiplies activations that are zero, and is made zero (bf16) or finite
-// (MXFP4: scale code 0) so that the product is exactly 0.
-template <int FMT>
-__device__ __forceinline__ bf16x8 w_operand(const WChunk<FMT>& w, int i, float scale, bool ok) {
-  if (FMT == W_BF16) {
-    const uint32_t m = ok ? ~0u : 0u;
-    const u32x4 v = w.q[i] & m;
-    return *(const bf16x8*)&v;
-  } else {
-    const uint32_t d = i == 0 ? w.q[0][0] : i == 1 ? w.q[0][1] : i == 2 ? w.q[0][2] : w.q[0][3];
-    return fp4x8_to_bf16(d, scale);
-  }
+// bf16 MFMA B operand i (8 K values) of a lane's block. A block past the row
+// end (!ok) multiplies activations that are zero, and is made zero so that the
+// product is exactly 0.
+__device__ __forceinline__ bf16x8 w_operand_bf16(const WChunk<W_BF16>& w, int i, bool ok) {
+  const uint32_t m = ok ? ~0u : 0u;
+  const u32x4 v = w.q[i] & m;
+  return *(const bf16x8*)&v;
+}
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// Block-scaled MFMA, 16 x 16 outputs, K 128: A e4m3 (cbsz 0), B e2m1 (blgp 4,
+// the upper half of the B registers unused), one e8m0 code per lane for each.
+__device__ __forceinline__ f32x4 mfma_fp8_fp4(const i32x8& a, const i32x8& b, f32x4 acc, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 4, 0, sa, 0, sb);
 }
 
 // Barrier that orders LDS accesses only: global loads stay in flight.
@@ -162,7 +216,10 @@ extern __shared__ __attribute__((aligned(16))) uint8_t skinny_scales[];
 template <int FMT, bool GATED, int SPT>
 __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
   using C = Cfg<FMT>;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * C::LROW];
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf[2][C::BUF_BYTES];
+  // MXFP4: per-wave region that rearranges a chunk's weights (2 streams x 4 steps)
+  constexpr int kWtStep = 16 * 64 + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t wtr[FMT == W_MXFP4 ? NW : 1][FMT == W_MXFP4 ? 8 * kWtStep : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int mt = blockIdx.x / p.n_tiles;
@@ -180,9 +237,30 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
   const int nb = nt * block_cols(GATED) + wave * (GATED ? 16 : 32);
   const bool wave_on = nb < N;  // idle waves still stage A and meet every barrier
   const int c0 = nb + l16, c1 = GATED ? c0 : nb + 16 + l16;
-  const size_t wr0 = (size_t)seg * N + min(c0, N - 1);
-  const size_t wr1 = (size_t)seg * N + min(c1, N - 1);
-  const void* B1 = GATED ? p.B1 : p.B0;
+  // weight rows of this segment as buffer resources; lane offsets: row, then
+  // block q of the first step (MXFP4: 16 bytes per block, bf16: 64)
+  const uint32_t rowbytes = FMT == W_MXFP4 ? K / 2 : 2 * K;
+  const uint32_t segbytes = (uint32_t)N * rowbytes;
+  const __amdgpu_buffer_rsrc_t rs0 = weight_rsrc((const uint8_t*)p.B0 + (size_t)seg * segbytes, segbytes);
+  const __amdgpu_buffer_rsrc_t rs1 =
+      weight_rsrc((const uint8_t*)(GATED ? p.B1 : p.B0) + (size_t)seg * segbytes, segbytes);
+  constexpr uint32_t BLOCK_BYTES = FMT == W_MXFP4 ? 16 : 64;
+  // bf16: lane (l16, q) loads its own blocks. MXFP4: a chunk is 256 bytes of
+  // each of a stream's 16 rows, loaded as 4 rows x 256 bytes per instruction
+  // (instruction j: row 4 j + q, bytes 16 l16), whole 128-byte lines per
+  // request, and rearranged through LDS into the MFMA operand layout.
+  uint32_t vo0[FMT == W_MXFP4 ? 4 : 1], vo1[FMT == W_MXFP4 ? 4 : 1];
+  if (FMT == W_MXFP4) {
+    const int b1 = GATED ? nb : nb + 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vo0[j] = (uint32_t)min(nb + 4 * j + q, N - 1) * rowbytes + 16 * l16;
+      vo1[j] = (uint32_t)min(b1 + 4 * j + q, N - 1) * rowbytes + 16 * l16;
+    }
+  } else {
+    vo0[0] = (uint32_t)min(c0, N - 1) * rowbytes + BLOCK_BYTES * q;
+    vo1[0] = (uint32_t)min(c1, N - 1) * rowbytes + BLOCK_BYTES * q;
+  }
 
   // MXFP4 scales of the workgroup's rows [n_lo, n_lo + RR) (GEMM1: gate in
   // LDS rows 0..63, up in 64..127), staged in LDS. Pieces past the valid rows
@@ -208,69 +286,140 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
     sc1 = skinny_scales + (size_t)((GATED ? RR : 0) + min(c1, N - 1) - n_lo) * KB;
   }
 
-  // This thread's A pieces: piece j covers tile row r_j, 8 K values at column
-  // 8 * pc of each chunk. Rows past the segment end re-read the last row (their
-  // results are never stored); K past the end is zeroed when written to LDS.
-  constexpr int PPR = C::KC / 8;  // pieces per row per chunk
+  // This thread's activation pieces. bf16: piece j covers tile row r_j, 8 K
+  // values at column 8 * pc of each chunk. Split (MXFP4): pieces of 16 hi
+  // bytes and the same 16 lo bytes at column 16 * pc of rows r_j, and threads
+  // 0..15 carry the 16 scale bytes of row tid. Rows past the segment end
+  // re-read the last row (their results are never stored); K past the end is
+  // zeroed when written to LDS (the split rows' scale codes there are 0).
+  constexpr bool QA = FMT == W_MXFP4;
+  constexpr int PPR = QA ? C::KC / 16 : C::KC / 8;  // pieces per row per chunk
+  constexpr int NP = QA ? C::QPPT : C::PPT;          // pieces per thread (per array)
+  constexpr int VPP = QA ? 16 : 8;                   // K values per piece
   const int pc = tid % PPR;
-  const uint16_t* a_src[C::PPT];
-  int a_lds[C::PPT];
+  size_t a_row[NP];
+  int a_lds[NP];
 #pragma unroll
-  for (int j = 0; j < C::PPT; ++j) {
+  for (int j = 0; j < NP; ++j) {
     const int r = (tid + NT * j) / PPR;
     const int rr = min(r, rows - 1);
-    const int ar = p.a_perm ? p.a_perm[row0 + rr] / p.a_div : row0 + rr;
-    a_src[j] = p.A + (size_t)ar * K + 8 * pc;
-    a_lds[j] = r * C::LROW + 8 * pc;
+    a_row[j] = (size_t)(p.a_perm ? p.a_perm[row0 + rr] / p.a_div : row0 + rr);
+    a_lds[j] = QA ? r * C::QROW + 16 * pc : (r * C::LROW + 8 * pc) * 2;
+  }
+  size_t s_row = 0;  // split rows: scale row of thread tid < 16
+  if (QA) {
+    const int rr = min(tid & 15, rows - 1);
+    s_row = (size_t)(p.a_perm ? p.a_perm[row0 + rr] / p.a_div : row0 + rr);
   }
 
-  auto load_a = [&](u32x4 (&ar)[C::PPT], int c) {
-    const int kc = min(c * C::KC, K - 8 - 8 * pc);  // clamped: always inside the row
-#pragma unroll
-    for (int j = 0; j < C::PPT; ++j) ar[j] = *(const u32x4*)(a_src[j] + kc);
+  struct ARegs {
+    u32x4 v[NP];
+    u32x4 l[QA ? NP : 1];
+    u32x4 s;
   };
-  auto store_a = [&](const u32x4 (&ar)[C::PPT], int buf, int c) {
-    const uint32_t m = c * C::KC + 8 * pc < K ? ~0u : 0u;
+  auto load_a = [&](ARegs& ar, int c) {
+    const int kc = min(c * C::KC + VPP * pc, K - VPP);  // clamped: always inside the row
 #pragma unroll
-    for (int j = 0; j < C::PPT; ++j) *(u32x4*)&sA[buf][a_lds[j]] = ar[j] & m;
+    for (int j = 0; j < NP; ++j) {
+      if (QA) {
+        ar.v[j] = *(const u32x4*)(p.Aq.hi + a_row[j] * K + kc);
+        ar.l[j] = *(const u32x4*)(p.Aq.lo + a_row[j] * K + kc);
+      } else {
+        ar.v[j] = *(const u32x4*)(p.A + a_row[j] * K + kc);
+      }
+    }
+    if (QA) ar.s = *(const u32x4*)(p.Aq.sc + s_row * p.Aq.sc_stride + 16 * c);
   };
+  auto store_a = [&](const ARegs& ar, int buf, int c) {
+    const uint32_t m = c * C::KC + VPP * pc < K ? ~0u : 0u;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      *(u32x4*)&sbuf[buf][a_lds[j]] = ar.v[j] & m;
+      if (QA) *(u32x4*)&sbuf[buf][BM * C::QROW + a_lds[j]] = ar.l[j] & m;
+    }
+    if (QA && tid < 16) *(u32x4*)&sbuf[buf][2 * BM * C::QROW + 16 * tid] = ar.s;
+  };
+  // step t = c * SPC + u covers blocks 4 t .. 4 t + 3 (4 BLOCK_BYTES bytes per row)
+  // Chunks past the last are loaded too (the loop below has no exits); their
+  // offset is moved past the segment, where buffer loads return 0 without a
+  // memory access.
   auto load_chunk = [&](WSet<FMT>& w, int c) {
+    const int so = c < nch ? c * C::SPC * 4 * BLOCK_BYTES : (int)segbytes;
 #pragma unroll
     for (int u = 0; u < C::SPC; ++u) {
-      const int kb = 4 * (c * C::SPC + u) + q;
-      load_w<FMT>(w.w0[u], p.B0, wr0, K, kb);
-      load_w<FMT>(w.w1[u], B1, wr1, K, kb);
+      if (FMT == W_MXFP4) {  // w.w0[u]: instruction u (rows 4 u + q)
+        w.w0[u].q[0] = __builtin_amdgcn_raw_buffer_load_b128(rs0, vo0[u], so, 0);
+        w.w1[u].q[0] = __builtin_amdgcn_raw_buffer_load_b128(rs1, vo1[u], so, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t o = 4 * BLOCK_BYTES * u + 16 * i;
+          w.w0[u].q[i] = __builtin_amdgcn_raw_buffer_load_b128(rs0, vo0[0] + o, so, 0);
+          w.w1[u].q[i] = __builtin_amdgcn_raw_buffer_load_b128(rs1, vo1[0] + o, so, 0);
+        }
+      }
     }
   };
 
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const WSet<FMT>& w, int buf, int c) {
     if (!wave_on) return;
-    const uint16_t* arow = &sA[buf][l16 * C::LROW + 32 * q];
+    if constexpr (QA) {
+      // rearrange: lane (l16, q) of instruction j holds row 4 j + q, block
+      // l16 of the chunk = step l16 / 4, lane group l16 % 4; the wave's
+      // region is [stream][step][row][group] x 16 bytes, steps padded by 16
+      // bytes against bank conflicts
+      uint8_t* wt = &wtr[wave][0];
 #pragma unroll
-    for (int u = 0; u < C::SPC; ++u) {
-      const int kb = 4 * (c * C::SPC + u) + q;
-      const bool ok = kb < KB;
-      u32x4 a[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *(const u32x4*)(arow + 128 * u + 8 * i);
-      float s0 = 1.f, s1 = 1.f;
-      if (FMT == W_MXFP4) {
-        const int kbc = min(kb, KB - 1);
-        s0 = e8m0_to_f32(ok ? (uint32_t)sc0[kbc] : 0u);
-        s1 = e8m0_to_f32(ok ? (uint32_t)sc1[kbc] : 0u);
+      for (int j = 0; j < C::SPC; ++j) {
+        const int o = (l16 >> 2) * kWtStep + (4 * j + q) * 64 + (l16 & 3) * 16;
+        *(u32x4*)(wt + o) = w.w0[j].q[0];
+        *(u32x4*)(wt + 4 * kWtStep + o) = w.w1[j].q[0];
       }
+      const uint8_t* hrow = &sbuf[buf][l16 * C::QROW];
+      const uint8_t* lrow = hrow + BM * C::QROW;
+      const uint8_t* srow = &sbuf[buf][2 * BM * C::QROW + 16 * l16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x8 av = *(const bf16x8*)&a[i];
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, w_operand<FMT>(w.w0[u], i, s0, ok), acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, w_operand<FMT>(w.w1[u], i, s1, ok), acc1, 0, 0, 0);
+      for (int u = 0; u < C::SPC; ++u) {
+        const int kbc = min(4 * (c * C::SPC + u) + q, KB - 1);
+        const u32x4 h0 = *(const u32x4*)(hrow + 128 * u + 16 * q);
+        const u32x4 h1 = *(const u32x4*)(hrow + 128 * u + 64 + 16 * q);
+        const u32x4 l0 = *(const u32x4*)(lrow + 128 * u + 16 * q);
+        const u32x4 l1 = *(const u32x4*)(lrow + 128 * u + 64 + 16 * q);
+        const i32x8 ah = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+        const i32x8 al = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
+        const int sa = srow[4 * u + q];
+        const int sb0 = sc0[kbc], sb1 = sc1[kbc];
+        const u32x4 c0w = *(const u32x4*)(wt + u * kWtStep + l16 * 64 + q * 16);
+        const u32x4 c1w = *(const u32x4*)(wt + (4 + u) * kWtStep + l16 * 64 + q * 16);
+        const i32x8 b0 = {(int)c0w[0], (int)c0w[1], (int)c0w[2], (int)c0w[3], 0, 0, 0, 0};
+        const i32x8 b1 = {(int)c1w[0], (int)c1w[1], (int)c1w[2], (int)c1w[3], 0, 0, 0, 0};
+        acc0 = mfma_fp8_fp4(ah, b0, acc0, sa, sb0);
+        acc1 = mfma_fp8_fp4(ah, b1, acc1, sa, sb1);
+        acc0 = mfma_fp8_fp4(al, b0, acc0, sa, sb0);
+        acc1 = mfma_fp8_fp4(al, b1, acc1, sa, sb1);
+      }
+    } else {
+      const uint16_t* arow = (const uint16_t*)&sbuf[buf][(l16 * C::LROW + 32 * q) * 2];
+#pragma unroll
+      for (int u = 0; u < C::SPC; ++u) {
+        const int kb = 4 * (c * C::SPC + u) + q;
+        const bool ok = kb < KB;
+        u32x4 a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = *(const u32x4*)(arow + 128 * u + 8 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8 av = *(const bf16x8*)&a[i];
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, w_operand_bf16(w.w0[u], i, ok), acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, w_operand_bf16(w.w1[u], i, ok), acc1, 0, 0, 0);
+        }
       }
     }
   };
 
   WSet<FMT> wx, wy;
-  u32x4 ar[C::PPT];
+  ARegs ar;
   load_a(ar, 0);
   load_chunk(wx, 0);
   if (FMT == W_MXFP4) {
@@ -281,31 +430,22 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
   store_a(ar, 0, 0);
   lds_barrier();
   // Chunk c: weights in wx, activations in buffer 0; chunk c + 1: wy, buffer 1.
-  // The loop body has no exits, so every load in it is unconditional and the
-  // compiler keeps exact wait counts: the next chunk stays in flight.
-  int c = 0;
-  for (; c + 2 < nch; c += 2) {
-    load_a(ar, c + 1);
-    load_chunk(wy, c + 1);
-    compute(wx, 0, c);
-    store_a(ar, 1, c + 1);
-    lds_barrier();
-    load_a(ar, c + 2);
-    load_chunk(wx, c + 2);
-    compute(wy, 1, c + 1);
-    store_a(ar, 0, c + 2);
-    lds_barrier();
+  // The loop runs whole pairs of chunks and has no exits, so every load in it
+  // is unconditional and the compiler keeps exact wait counts: the next chunk
+  // stays in flight. A step past the last chunk only meets the barrier.
+#define MOE_SKINNY_STEP(wcur, wnext, cc)                    \
+  {                                                         \
+    load_a(ar, (cc) + 1);                                   \
+    load_chunk(wnext, (cc) + 1);                            \
+    if ((cc) < nch) compute(wcur, (cc) & 1, cc);            \
+    store_a(ar, ((cc) + 1) & 1, (cc) + 1);                  \
+    lds_barrier();                                          \
   }
-  if (c + 1 < nch) {
-    load_a(ar, c + 1);
-    load_chunk(wy, c + 1);
-    compute(wx, 0, c);
-    store_a(ar, 1, c + 1);
-    lds_barrier();
-    compute(wy, 1, c + 1);
-  } else {
-    compute(wx, 0, c);
+  for (int c = 0; c < nch; c += 2) {
+    MOE_SKINNY_STEP(wx, wy, c)
+    MOE_SKINNY_STEP(wy, wx, c + 1)
   }
+#undef MOE_SKINNY_STEP
 
   // 16x16 result layout: lane holds column (lane & 15), rows 4 (lane >> 4) + r.
   if (!wave_on) return;

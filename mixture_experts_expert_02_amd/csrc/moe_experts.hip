@@ -54,7 +54,7 @@ struct Plan {
   int chunk, nch;
   // byte offsets
   size_t status, counts, cu, offsets, tile_seg, tile_row0, blkcnt, blkbad, perm, inv_perm, w_sorted, act,
-      y, total;
+      xq, aq, y, total;
 };
 
 int check_problem(const moe_problem* p, bool grouped) {
@@ -73,6 +73,10 @@ int check_problem(const moe_problem* p, bool grouped) {
   if (p->E > kMaxExperts) return MOE_ENOTSUP;
   const long long rows = grouped ? (long long)p->T : (long long)p->T * p->k;
   if (rows > (1LL << 30)) return MOE_ENOTSUP;
+  // The kernels address activation rows and one expert's weights with 32-bit
+  // byte offsets: T*H and rows*I below 2^31 elements, I*H at most 2^30.
+  if ((long long)p->T * p->H >= (1LL << 31) || rows * p->I >= (1LL << 31) || (long long)p->I * p->H > (1LL << 30))
+    return MOE_ENOTSUP;
   return MOE_OK;
 }
 
@@ -87,6 +91,10 @@ int max_split_k() {
 // Workspace layout of problem p. The y buffer comes last and holds s_cap
 // partial outputs; with ws_bytes given, s_cap shrinks to what fits, so a
 // workspace sized for a larger T (fewer K ranges, more rows) still serves.
+size_t quant_bytes(long long R, int K) {
+  return (size_t)R * (2ull * K + moe::skinny::quant_sc_stride(K));
+}
+
 Plan make_plan(const moe_problem& p, bool grouped, size_t ws_bytes = ~(size_t)0) {
   Plan pl{};
   pl.M = grouped ? (long long)p.T : (long long)p.T * p.k;
@@ -126,6 +134,10 @@ Plan make_plan(const moe_problem& p, bool grouped, size_t ws_bytes = ~(size_t)0)
     pl.w_sorted = take(4ull * pl.M);
   }
   pl.act = take(2ull * pl.M * p.I);
+  if (p.wfmt == MOE_W_MXFP4) {  // activation rows split for the block-scaled MFMA
+    pl.xq = take(quant_bytes(p.T, p.H));
+    pl.aq = take(quant_bytes(pl.M, p.I));
+  }
   if (!grouped) {
     pl.y = o;
     const size_t one = 2ull * pl.M * p.H;
@@ -140,6 +152,22 @@ Plan make_plan(const moe_problem& p, bool grouped, size_t ws_bytes = ~(size_t)0)
 template <typename T>
 T* at(void* base, size_t off) {
   return (T*)((char*)base + off);
+}
+
+// hi and lo bytes, then scale rows, of R split activation rows of K values
+moe::skinny::QRows quant_rows_at(void* base, size_t off, long long R, int K) {
+  moe::skinny::QRows q;
+  q.hi = at<uint8_t>(base, off);
+  q.lo = q.hi + (size_t)R * K;
+  q.sc = q.lo + (size_t)R * K;
+  q.sc_stride = moe::skinny::quant_sc_stride(K);
+  return q;
+}
+
+int launch_quant(const void* src, long long R, int K, const moe::skinny::QRows& q, hipStream_t s) {
+  if (R <= 0) return MOE_OK;
+  hipLaunchKernelGGL(moe::skinny::k_quant_rows, dim3((unsigned)R), dim3(256), 0, s, (const uint16_t*)src, (int)R, K, q);
+  return MOE_OK;
 }
 
 moe::ActParams act_params(const moe_problem& p) {
@@ -244,6 +272,7 @@ struct GemmIO {
   const float* row_w;
   int s_cap;         // GEMM2: K ranges with room in C (1 = C is [rows, N])
   long long c_split; // elements between partial outputs
+  moe::skinny::QRows Aq;  // A split for the block-scaled MFMA (MXFP4 weights)
 };
 
 template <bool GATED>
@@ -255,6 +284,7 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
   if (pl.skinny) {
     moe::skinny::Params q;
     q.A = (const uint16_t*)io.A;
+    q.Aq = io.Aq;
     q.a_perm = io.a_perm;
     q.a_div = io.a_div;
     q.B0 = io.B0;
@@ -361,14 +391,19 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
   mark(0);
   if ((rc = launch_align(ids, tw, M, p->E, pl.BM, pl, o, ws, s))) return rc;
 
-  GemmIO g1{x, o.perm, p->k, wg, wu, sg, su, p->I, p->H, at<void>(ws, pl.act), o.w_sorted, 1, 0};
+  const bool mx = p->wfmt == MOE_W_MXFP4;
+  GemmIO g1{x, o.perm, p->k, wg, wu, sg, su, p->I, p->H, at<void>(ws, pl.act), o.w_sorted, 1, 0, {}};
+  if (mx) g1.Aq = quant_rows_at(ws, pl.xq, p->T, p->H);
   mark(1);
+  if (mx) launch_quant(x, p->T, p->H, g1.Aq, s);
   if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
 
   const long long y_split = pl.M * p->H;
   GemmIO g2{at<void>(ws, pl.act), nullptr, 1, wd, nullptr, sd, nullptr, p->H, p->I, at<void>(ws, pl.y), nullptr,
-            pl.s_cap, y_split};
+            pl.s_cap, y_split, {}};
+  if (mx) g2.Aq = quant_rows_at(ws, pl.aq, pl.M, p->I);
   mark(2);
+  if (mx) launch_quant(g2.A, pl.M, p->I, g2.Aq, s);
   if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
 
   mark(3);
@@ -492,9 +527,18 @@ int moe_experts_forward_grouped(const moe_problem* p, const void* x_nvs, const i
   hipLaunchKernelGGL(moe::k_grouped_prep, dim3(1), dim3(1024), (size_t)(3 * p->E + 32) * 4, s, cu_seqlens, p->E,
                      p->T, pl.BM, o);
   if ((rc = launch_status())) return rc;
-  GemmIO g1{x_nvs, nullptr, 1, w_gate, w_up, s_gate, s_up, p->I, p->H, at<void>(ws, pl.act), route_w, 1, 0};
+  const bool mx = p->wfmt == MOE_W_MXFP4;
+  GemmIO g1{x_nvs, nullptr, 1, w_gate, w_up, s_gate, s_up, p->I, p->H, at<void>(ws, pl.act), route_w, 1, 0, {}};
+  if (mx) {
+    g1.Aq = quant_rows_at(ws, pl.xq, p->T, p->H);
+    launch_quant(x_nvs, p->T, p->H, g1.Aq, s);
+  }
   if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
-  GemmIO g2{at<void>(ws, pl.act), nullptr, 1, w_down, nullptr, s_down, nullptr, p->H, p->I, out_nvs, nullptr, 1, 0};
+  GemmIO g2{at<void>(ws, pl.act), nullptr, 1, w_down, nullptr, s_down, nullptr, p->H, p->I, out_nvs, nullptr, 1, 0, {}};
+  if (mx) {
+    g2.Aq = quant_rows_at(ws, pl.aq, pl.M, p->I);
+    launch_quant(g2.A, pl.M, p->I, g2.Aq, s);
+  }
   if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
   hipLaunchKernelGGL(moe::k_zero_tail, dim3(p->T), dim3(256), 0, s, (uint16_t*)out_nvs,
                      (const int32_t*)o.status, p->T, p->H);

@@ -80,6 +80,9 @@ def test_workspace_room_for_split_down_projection(monkeypatch):
     (dict(act="swiglu_oai", alpha=math.nan, limit=7.0), B.MOE_EINVAL),
     (dict(wfmt="mxfp4", H=16448), B.MOE_ENOTSUP),  # MXFP4 scale rows beyond the LDS staging limit
     (dict(wfmt="mxfp4", I=16448), B.MOE_ENOTSUP),
+    (dict(T=1 << 20, H=2048, I=256), B.MOE_ENOTSUP),  # T*H = 2^31: beyond 32-bit row offsets
+    (dict(T=1 << 18, k=2, H=128, I=4096), B.MOE_ENOTSUP),  # rows*I = 2^31
+    (dict(H=32768, I=32832), B.MOE_ENOTSUP),      # one expert's I*H above 2^30
 ])
 def test_invalid_problems_rejected(kw, code):
     base = dict(T=16, H=128, I=256, E=8, k=2)

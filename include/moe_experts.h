@@ -126,7 +126,7 @@ int moe_experts_workspace_layout(const moe_problem* p, moe_ws_layout* layout);
  *   w_down       (device) [E, H, I] bf16, or MXFP4 codes [E, H, I/2]
  *   s_gate, s_up, s_down (device) e8m0 scales [E, N, K/32] for MXFP4, NULL for bf16
  *                x, weights, scales and out 16-byte aligned (else MOE_EINVAL);
- *                MXFP4 needs H, I <= 16384; T*H and T*k*I must stay below 2^31
+ *                MXFP4 needs H, I <= 16384; T*H and T*k*max(H, I) must stay below 2^31
  *                and I*H at most 2^30 (else MOE_ENOTSUP)
  *   out          (device) bf16 [T, H], overwritten:
  *                out[t] = sum over j = 0..k-1, in that order, in fp32, of

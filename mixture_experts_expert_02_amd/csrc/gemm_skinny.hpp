@@ -105,17 +105,21 @@ struct Params {
   ActParams act;
 };
 
-// One workgroup per row, one 32-value block per thread.
-__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ src, int rows, int K, QRows q) {
+// One workgroup per row, one 32-value block per thread. With perm, output
+// row r is source row perm[r] / div (sorted row -> token), for the first
+// status[1] rows (the valid sorted rows; the rest are never read).
+__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ src, int rows, int K, QRows q,
+                                                    const int32_t* perm, int div, const int32_t* status) {
   const int r = blockIdx.x;
-  if (r >= rows) return;
+  if (r >= rows || (perm && r >= status[1])) return;
+  const size_t sr = perm ? (size_t)(perm[r] / div) : (size_t)r;
   const int KB = K / 32;
   for (int b = threadIdx.x; b < q.sc_stride; b += 256) {
     if (b >= KB) {
       q.sc[(size_t)r * q.sc_stride + b] = 0;
       continue;
     }
-    const u32x4* in = (const u32x4*)(src + (size_t)r * K + 32 * b);
+    const u32x4* in = (const u32x4*)(src + sr * K + 32 * b);
     uint32_t w[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -420,8 +424,8 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
 
   WSet<FMT> wx, wy;
   ARegs ar;
-  load_a(ar, 0);
   load_chunk(wx, 0);
+  load_a(ar, 0);
   if (FMT == W_MXFP4) {
 #pragma unroll
     for (int j = 0; j < SPT; ++j)

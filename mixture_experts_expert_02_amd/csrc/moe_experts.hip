@@ -74,8 +74,9 @@ int check_problem(const moe_problem* p, bool grouped) {
   const long long rows = grouped ? (long long)p->T : (long long)p->T * p->k;
   if (rows > (1LL << 30)) return MOE_ENOTSUP;
   // The kernels address activation rows and one expert's weights with 32-bit
-  // byte offsets: T*H and rows*I below 2^31 elements, I*H at most 2^30.
-  if ((long long)p->T * p->H >= (1LL << 31) || rows * p->I >= (1LL << 31) || (long long)p->I * p->H > (1LL << 30))
+  // byte offsets: T*H and rows*max(H, I) below 2^31 elements, I*H at most 2^30.
+  if ((long long)p->T * p->H >= (1LL << 31) || rows * std::max(p->H, p->I) >= (1LL << 31) ||
+      (long long)p->I * p->H > (1LL << 30))
     return MOE_ENOTSUP;
   return MOE_OK;
 }
@@ -134,8 +135,8 @@ Plan make_plan(const moe_problem& p, bool grouped, size_t ws_bytes = ~(size_t)0)
     pl.w_sorted = take(4ull * pl.M);
   }
   pl.act = take(2ull * pl.M * p.I);
-  if (p.wfmt == MOE_W_MXFP4) {  // activation rows split for the block-scaled MFMA
-    pl.xq = take(quant_bytes(p.T, p.H));
+  if (p.wfmt == MOE_W_MXFP4) {  // activation rows split for the block-scaled MFMA, sorted order
+    pl.xq = take(quant_bytes(pl.M, p.H));
     pl.aq = take(quant_bytes(pl.M, p.I));
   }
   if (!grouped) {
@@ -164,9 +165,13 @@ moe::skinny::QRows quant_rows_at(void* base, size_t off, long long R, int K) {
   return q;
 }
 
-int launch_quant(const void* src, long long R, int K, const moe::skinny::QRows& q, hipStream_t s) {
+// Split R activation rows; with perm, row r comes from source row perm[r] / div
+// (the first status[1] rows).
+int launch_quant(const void* src, long long R, int K, const moe::skinny::QRows& q, hipStream_t s,
+                 const int32_t* perm = nullptr, int div = 1, const int32_t* status = nullptr) {
   if (R <= 0) return MOE_OK;
-  hipLaunchKernelGGL(moe::skinny::k_quant_rows, dim3((unsigned)R), dim3(256), 0, s, (const uint16_t*)src, (int)R, K, q);
+  hipLaunchKernelGGL(moe::skinny::k_quant_rows, dim3((unsigned)R), dim3(256), 0, s, (const uint16_t*)src, (int)R, K, q,
+                     perm, div, status);
   return MOE_OK;
 }
 
@@ -393,9 +398,12 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
 
   const bool mx = p->wfmt == MOE_W_MXFP4;
   GemmIO g1{x, o.perm, p->k, wg, wu, sg, su, p->I, p->H, at<void>(ws, pl.act), o.w_sorted, 1, 0, {}};
-  if (mx) g1.Aq = quant_rows_at(ws, pl.xq, p->T, p->H);
+  if (mx) {  // x split in sorted row order: GEMM1 reads its rows without the permutation
+    g1.Aq = quant_rows_at(ws, pl.xq, pl.M, p->H);
+    g1.a_perm = nullptr;
+  }
   mark(1);
-  if (mx) launch_quant(x, p->T, p->H, g1.Aq, s);
+  if (mx) launch_quant(x, pl.M, p->H, g1.Aq, s, o.perm, p->k, o.status);
   if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
 
   const long long y_split = pl.M * p->H;
@@ -530,8 +538,8 @@ int moe_experts_forward_grouped(const moe_problem* p, const void* x_nvs, const i
   const bool mx = p->wfmt == MOE_W_MXFP4;
   GemmIO g1{x_nvs, nullptr, 1, w_gate, w_up, s_gate, s_up, p->I, p->H, at<void>(ws, pl.act), route_w, 1, 0, {}};
   if (mx) {
-    g1.Aq = quant_rows_at(ws, pl.xq, p->T, p->H);
-    launch_quant(x_nvs, p->T, p->H, g1.Aq, s);
+    g1.Aq = quant_rows_at(ws, pl.xq, pl.M, p->H);
+    launch_quant(x_nvs, pl.M, p->H, g1.Aq, s);
   }
   if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
   GemmIO g2{at<void>(ws, pl.act), nullptr, 1, w_down, nullptr, s_down, nullptr, p->H, p->I, out_nvs, nullptr, 1, 0, {}};

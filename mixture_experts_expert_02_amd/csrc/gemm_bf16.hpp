@@ -21,9 +21,11 @@
 // all of its loads before each stage barrier; 64 K per stage keeps the
 // barriers and the load instructions per MFMA few. The 16-byte chunks of
 // every row are XOR-swizzled so that the MFMA operand reads are bank-conflict
-// free. In a partial row tile the rows past the segment end
-// load a valid row of the tile and their results are dropped; waves whose
-// 128 rows are all past the end skip their MFMAs.
+// free. In a partial row tile, 8-row blocks of A that lie past the segment
+// end are not loaded (their rows of the product are garbage and dropped, and
+// a row of the product depends on its own A row only), the other rows past
+// the end load a valid row of the tile; waves whose 128 rows are all past
+// the end skip their MFMAs.
 #pragma once
 
 #include "common.hpp"
@@ -191,10 +193,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
 #define MOE_BIG_DMA(st, kbytes, q)                                                                           \
   {                                                                                                          \
     const int qq = (q) & 3;                                                                                  \
-    if ((q) < 4)                                                                                             \
-      __builtin_amdgcn_global_load_lds(Ab + (a_off[qq] + (kbytes)),                                          \
-                                       &smem[(st) * 2 * STAGE_U4 + (wave * 4 + qq) * 64], 16, 0, 0);          \
-    else                                                                                                     \
+    if ((q) < 4) {                                                                                           \
+      if (wave * 32 + qq * 8 < rows)                                                                         \
+        __builtin_amdgcn_global_load_lds(Ab + (a_off[qq] + (kbytes)),                                        \
+                                         &smem[(st) * 2 * STAGE_U4 + (wave * 4 + qq) * 64], 16, 0, 0);        \
+    } else                                                                                                   \
       __builtin_amdgcn_global_load_lds(Bw + (b_off[qq] + (kbytes)),                                          \
                                        &smem[(st) * 2 * STAGE_U4 + STAGE_U4 + (wave * 4 + qq) * 64], 16, 0, 0); \
   }

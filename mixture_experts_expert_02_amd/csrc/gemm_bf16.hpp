@@ -246,7 +246,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   }
   // MFMAs 2k, 2k+1 of an 8-MFMA batch (A fragment k, B fragments 0 and 1)
 #define MOE_BIG_MFMA2(dA, dB, k)                                                                    \
-  if (active) {                                                                                     \
+  if (ACT_) {                                                                                       \
     acc[k][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA[k], dB[0], acc[k][0], 0, 0, 0);          \
     acc[k][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA[k], dB[1], acc[k][1], 0, 0, 0);          \
   }
@@ -286,30 +286,46 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   // stage s+1 (issued two substeps earlier; only vmcnt(0) orders direct-to-LDS
   // loads reliably) and meets the others at the barrier; the reads of
   // (s+1, 0) then go with the remaining MFMA pairs.
-  int st = 0;
-  for (int s = 0; s < KT; ++s) {
-    const int stn = st ^ 1;
-    const bool load = s + 1 < KT;
-    const uint32_t kl = (uint32_t)(s + 1) * BK * 2u;
-    MOE_BIG_SUBSTEP(fa, fb, ga, gb, st, 1, true, load, 0)
-    MOE_BIG_SUBSTEP(ga, gb, fa, fb, st, 2, true, false, 0)
-    MOE_BIG_SUBSTEP(fa, fb, ga, gb, st, 3, true, false, 0)
-    MOE_LGKM_WAIT_TIE(ga, gb);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (load && k >= 1) {
-        MOE_BIG_READ1(fa, fb, stn, 0, 2 * (k - 1))
-        MOE_BIG_READ1(fa, fb, stn, 0, 2 * (k - 1) + 1)
-      }
-      MOE_BIG_MFMA2(ga, gb, k)
-      __builtin_amdgcn_sched_barrier(0);
-      if (load && k == 0) {
-        wait_vmcnt<0>();
-        stage_barrier();
-      }
-    }
-    st = stn;
+  // one stage; LOAD: stage s + 1 exists (its loads are issued here)
+#define MOE_BIG_STAGE(LOAD)                                      \
+  {                                                              \
+    const int stn = st ^ 1;                                      \
+    const uint32_t kl = (uint32_t)(s + 1) * BK * 2u;             \
+    MOE_BIG_SUBSTEP(fa, fb, ga, gb, st, 1, true, LOAD, 0)        \
+    MOE_BIG_SUBSTEP(ga, gb, fa, fb, st, 2, true, false, 0)       \
+    MOE_BIG_SUBSTEP(fa, fb, ga, gb, st, 3, true, false, 0)       \
+    MOE_LGKM_WAIT_TIE(ga, gb);                                   \
+    _Pragma("unroll") for (int k = 0; k < 4; ++k) {              \
+      if (LOAD && k >= 1) {                                      \
+        MOE_BIG_READ1(fa, fb, stn, 0, 2 * (k - 1))               \
+        MOE_BIG_READ1(fa, fb, stn, 0, 2 * (k - 1) + 1)           \
+      }                                                          \
+      MOE_BIG_MFMA2(ga, gb, k)                                   \
+      __builtin_amdgcn_sched_barrier(0);                         \
+      if (LOAD && k == 0) {                                      \
+        wait_vmcnt<0>();                                         \
+        stage_barrier();                                         \
+      }                                                          \
+    }                                                            \
+    st = stn;                                                    \
   }
+  // The K loop exists twice, for waves with and without rows (ACT_), and its
+  // last stage is peeled, so the loop body has no branches.
+#define MOE_BIG_KLOOP                                            \
+  {                                                              \
+    int st = 0, s = 0;                                           \
+    for (; s + 1 < KT; ++s) MOE_BIG_STAGE(true)                  \
+    MOE_BIG_STAGE(false)                                         \
+  }
+  if (active) {
+    constexpr bool ACT_ = true;
+    MOE_BIG_KLOOP
+  } else {
+    constexpr bool ACT_ = false;
+    MOE_BIG_KLOOP
+  }
+#undef MOE_BIG_KLOOP
+#undef MOE_BIG_STAGE
 #undef MOE_BIG_DMA
 #undef MOE_DSR
 #undef MOE_BIG_READ1

@@ -293,9 +293,12 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
   // This thread's activation pieces. bf16: piece j covers tile row r_j, 8 K
   // values at column 8 * pc of each chunk. Split (MXFP4): pieces of 16 hi
   // bytes and the same 16 lo bytes at column 16 * pc of rows r_j, and threads
-  // 0..15 carry the 16 scale bytes of row tid. Rows past the segment end
-  // re-read the last row (their results are never stored); K past the end is
-  // zeroed when written to LDS (the split rows' scale codes there are 0).
+  // 0..15 carry the 16 scale bytes of row tid. Rows past the segment end are
+  // not loaded but written to LDS as zeros (their results are never stored;
+  // decode tiles hold one or two live rows, and loading the other fourteen
+  // would spend the compute unit's outstanding-request slots, which the
+  // weight stream needs); K past the end is zeroed when written to LDS (the
+  // split rows' scale codes there are 0).
   constexpr bool QA = FMT == W_MXFP4;
   constexpr int PPR = QA ? C::KC / 16 : C::KC / 8;  // pieces per row per chunk
   constexpr int NP = QA ? C::QPPT : C::PPT;          // pieces per thread (per array)
@@ -303,10 +306,12 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
   const int pc = tid % PPR;
   size_t a_row[NP];
   int a_lds[NP];
+  bool a_live[NP];
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     const int r = (tid + NT * j) / PPR;
     const int rr = min(r, rows - 1);
+    a_live[j] = r < rows;
     a_row[j] = (size_t)(p.a_perm ? p.a_perm[row0 + rr] / p.a_div : row0 + rr);
     a_lds[j] = QA ? r * C::QROW + 16 * pc : (r * C::LROW + 8 * pc) * 2;
   }
@@ -325,11 +330,15 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
     const int kc = min(c * C::KC + VPP * pc, K - VPP);  // clamped: always inside the row
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
-      if (QA) {
-        ar.v[j] = *(const u32x4*)(p.Aq.hi + a_row[j] * K + kc);
-        ar.l[j] = *(const u32x4*)(p.Aq.lo + a_row[j] * K + kc);
-      } else {
-        ar.v[j] = *(const u32x4*)(p.A + a_row[j] * K + kc);
+      ar.v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (QA) ar.l[j] = u32x4{0u, 0u, 0u, 0u};
+      if (a_live[j]) {
+        if (QA) {
+          ar.v[j] = *(const u32x4*)(p.Aq.hi + a_row[j] * K + kc);
+          ar.l[j] = *(const u32x4*)(p.Aq.lo + a_row[j] * K + kc);
+        } else {
+          ar.v[j] = *(const u32x4*)(p.A + a_row[j] * K + kc);
+        }
       }
     }
     if (QA) ar.s = *(const u32x4*)(p.Aq.sc + s_row * p.Aq.sc_stride + 16 * c);

@@ -30,7 +30,7 @@ import torch
 __all__ = [
     "Workload", "WORKLOADS", "workload", "seed_for", "make_routing",
     "make_x", "make_bf16_weights", "make_mxfp4_weights", "make_pregrouped_layout",
-    "make_route_weights_nvs", "expert_weight", "bf16_to_f32",
+    "make_route_weights_nvs", "expert_weight", "bf16_to_f32", "make_logits", "make_router_bias",
 ]
 
 
@@ -127,6 +127,25 @@ def make_routing(wl: Workload, seed: int = 0, T: Optional[int] = None):
     psel = np.take_along_axis(p, order, axis=1)
     w = psel / psel.sum(axis=1, keepdims=True)
     return order.astype(np.int32), w.astype(np.float32)
+
+
+def make_logits(wl: Workload, seed: int = 0, T: Optional[int] = None) -> np.ndarray:
+    """Router logits float32 [T, E]: the same seeded N(0,1) draw as make_routing
+    (plus its Zipf expert bias on skewed workloads), rounded to float32."""
+    T = wl.T if T is None else T
+    rng = np.random.Generator(np.random.PCG64(seed_for(wl, "logits", 0, seed)))
+    logits = rng.standard_normal((T, wl.E))
+    if wl.zipf_s is not None:
+        prng = np.random.Generator(np.random.PCG64(seed_for(wl, "zipf", 0, seed)))
+        ranks = prng.permutation(wl.E) + 1
+        logits = logits - wl.zipf_s * np.log(ranks.astype(np.float64))[None, :]
+    return logits.astype(np.float32)
+
+
+def make_router_bias(wl: Workload, seed: int = 0, scale: float = 0.1) -> np.ndarray:
+    """Score-correction bias float32 [E] ~ N(0, scale^2) for grouped routing."""
+    rng = np.random.Generator(np.random.PCG64(seed_for(wl, "router_bias", 0, seed)))
+    return (scale * rng.standard_normal(wl.E)).astype(np.float32)
 
 
 # ----------------------------------------------------------------- activations

@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--print-source-hash", action="store_true")
+    ap.add_argument("--router", action="store_true",
+                    help="run the router (moe_route, Renormalize) on the workload's logits inside each step")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -52,6 +54,10 @@ class HipEvents:
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, ev, stream):
+        assert self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream.cuda_stream)) == 0
 
     def create(self, n):
         evs = []
@@ -193,7 +199,18 @@ def main():
     stream = torch.cuda.current_stream()
     hev = HipEvents()
 
-    def step(evs=()):
+    if args.router:
+        # the workload's ids and weights are this same Renormalize routing of these logits
+        logits_d = torch.from_numpy(synth.make_logits(wl)).to(dev)
+        rp = B.route_problem(wl.T, wl.E, wl.k, "renormalize")
+
+    def step(evs=(), rev=None):
+        if args.router:
+            if rev is not None:
+                hev.record(rev, stream)
+            rc = B.moe_route(rp, logits_d, None, ids_d, w_d, stream=stream)
+            if rc != 0:
+                raise B.MoeError(rc, "moe_route")
         rc = B.moe_experts_forward_timed(p, x, ids_d, w_d, *W, *S, out, ws, list(evs), stream=stream)
         if rc != 0:
             raise B.MoeError(rc, "moe_experts_forward_timed")
@@ -209,19 +226,24 @@ def main():
 
     K = args.steps
     evs = [hev.create(5) for _ in range(K)]
+    revs = hev.create(K) if args.router else [None] * K
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(evs[i])
+        step(evs[i], revs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage_ms = {s: [] for s in STAGES}
-    for e in evs:
+    stage_ms = {s: [] for s in (("router",) if args.router else ()) + STAGES}
+    for e, r in zip(evs, revs):
         for j, s in enumerate(STAGES):
             stage_ms[s].append(hev.elapsed_ms(e[j], e[j + 1]))
-    step_ms = [hev.elapsed_ms(e[0], e[4]) for e in evs]
+        if args.router:
+            stage_ms["router"].append(hev.elapsed_ms(r, e[0]))
+    step_ms = [hev.elapsed_ms(r if args.router else e[0], e[4]) for e, r in zip(evs, revs)]
     for e in evs:
         hev.destroy(e)
+    if args.router:
+        hev.destroy(revs)
     ms_per_step = wall * 1e3 / K
 
     M = wl.T * wl.k
@@ -257,6 +279,13 @@ def main():
         "event_ms_per_step": round(float(np.mean(step_ms)), 4),
         "roofline": roof,
     }
+    if args.router:
+        rbytes = wl.T * wl.E * 4 + wl.T * wl.k * 8
+        gbs = rbytes / (avg["router"] * 1e-3) / 1e9
+        res["config"]["router"] = "renormalize"
+        res["router"] = {"kernel": "k_route (Renormalize)", "us": round(avg["router"] * 1e3, 2),
+                         "algorithmic_bytes": rbytes, "achieved": round(gbs, 1), "unit": "GB/s",
+                         "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "bound": "hbm"}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, x, ids, w, W, S, args.cpu_sample_tokens)

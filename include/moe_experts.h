@@ -1,7 +1,8 @@
 /*
  * moe_experts.h — C ABI of the MI355X (gfx950) MoE experts library.
  *
- * The library runs the experts step of a mixture-of-experts layer on one GPU:
+ * The library runs the experts step of a mixture-of-experts layer on one GPU
+ * (and, optionally, the router step before it, moe_route):
  * group the router's top-k slots by expert (histogram, prefix sum to segment
  * end offsets, stable permutation), a grouped GEMM for the gate and up
  * projections with the activation and route weight applied in its epilogue,
@@ -194,6 +195,51 @@ int moe_experts_forward_grouped(const moe_problem* p, const void* x_nvs, const i
                                 const void* w_down, const uint8_t* s_gate, const uint8_t* s_up,
                                 const uint8_t* s_down, void* out_nvs, void* workspace,
                                 size_t workspace_bytes, moe_stream_t stream);
+
+/*
+ * Router step: per-token expert logits -> the top-k expert ids and route
+ * weights that moe_experts_forward takes.
+ * trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsMonolithic (router and experts in
+ * one call): _supports_routing_method names Renormalize, RenormalizeNaive and
+ * DeepSeekV3; apply passes the score-correction bias, the number of expert
+ * groups, the groups kept (topk_group) and the routed scaling factor. The page
+ * prints no formulas; the library reads them as:
+ *   MOE_ROUTE_RENORMALIZE (also RenormalizeNaive, which differs only in
+ *     evaluation order): w_j = exp(l_j) / sum over the k picks of exp(l_i),
+ *     the picks being the k largest logits.
+ *   MOE_ROUTE_DEEPSEEK_V3 (DeepSeek-V3 gating): s = sigmoid(l), selection
+ *     score s + bias; with n_group > 1 the E experts form n_group contiguous
+ *     groups, a group scores the sum of its two largest selection scores and
+ *     only the topk_group best groups stay eligible; the k largest selection
+ *     scores are picked and w_j = scale * s_j / sum of the picked s (0 if that
+ *     sum is 0).
+ * Ties go to the lower index; output slots are in descending selection score.
+ * Logits are clamped to the finite float32 range first (NaN = most negative).
+ * DeepSeekV3 scores are sigmoid evaluated in double and rounded to float,
+ * selection scores float adds, so picks are reproducible bit for bit.
+ *   logits       (device) float32 [T, E]
+ *   bias         (device) float32 [E], finite, or NULL (DeepSeekV3 only; ignored
+ *                otherwise)
+ *   topk_ids     (device) int32 [T, k], overwritten
+ *   topk_weights (device) float32 [T, k], overwritten
+ * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 32) (MOE_ENOTSUP beyond 1024 or 32,
+ * MOE_EINVAL for k > E); DeepSeekV3 with n_group > 1 needs n_group <= 64,
+ * E % n_group == 0, E / n_group >= 2, 1 <= topk_group <= n_group and
+ * k <= topk_group * E / n_group (MOE_EINVAL otherwise). No workspace; nothing
+ * is allocated.
+ */
+typedef enum { MOE_ROUTE_RENORMALIZE = 0, MOE_ROUTE_DEEPSEEK_V3 = 1 } moe_route_method;
+
+typedef struct {
+  int32_t T, E, k;
+  moe_route_method method;
+  int32_t n_group;              /* DeepSeekV3: 0 or 1 = no group limit */
+  int32_t topk_group;           /* DeepSeekV3 with n_group > 1 */
+  float routed_scaling_factor;  /* DeepSeekV3: weights multiplied by it (1 = none) */
+} moe_route_problem;
+
+int moe_route(const moe_route_problem* p, const float* logits, const float* bias, int32_t* topk_ids,
+              float* topk_weights, moe_stream_t stream);
 
 /* Reads the device status word of a workspace used by moe_experts_forward,
  * moe_experts_forward_grouped or moe_align: *n_bad = number of expert ids

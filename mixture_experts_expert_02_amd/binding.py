@@ -27,8 +27,10 @@ EXPORTED = (
     "moe_experts_workspace_bytes", "moe_experts_workspace_layout", "moe_experts_forward",
     "moe_experts_forward_timed", "moe_align_workspace_bytes", "moe_align",
     "moe_experts_grouped_workspace_bytes", "moe_experts_forward_grouped", "moe_device_error",
-    "moe_strerror",
+    "moe_strerror", "moe_route",
 )
+MOE_ROUTE_RENORMALIZE, MOE_ROUTE_DEEPSEEK_V3 = 0, 1
+_ROUTE = {"renormalize": MOE_ROUTE_RENORMALIZE, "deepseek_v3": MOE_ROUTE_DEEPSEEK_V3}
 
 
 class MoeProblem(ctypes.Structure):
@@ -36,6 +38,12 @@ class MoeProblem(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("wfmt", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
                 ("limit", ctypes.c_float)]
+
+
+class MoeRouteProblem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("method", ctypes.c_int32), ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
+                ("routed_scaling_factor", ctypes.c_float)]
 
 
 class MoeWsLayout(ctypes.Structure):
@@ -80,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.moe_experts_forward_grouped.restype = ctypes.c_int
         L.moe_device_error.argtypes = [vp, ctypes.POINTER(i32)]
         L.moe_device_error.restype = ctypes.c_int
+        L.moe_route.argtypes = [ctypes.POINTER(MoeRouteProblem), vp, vp, vp, vp, vp]
+        L.moe_route.restype = ctypes.c_int
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -169,6 +179,11 @@ def moe_strerror(status: int) -> str:
     return strerror(status)
 
 
+def moe_route(p: MoeRouteProblem, logits, bias, topk_ids, topk_weights, stream=None) -> int:
+    return lib().moe_route(ctypes.byref(p), _ptr(logits), _ptr(bias), _ptr(topk_ids), _ptr(topk_weights),
+                           _stream(stream))
+
+
 # ---------------------------------------------------------------- torch conveniences
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     """A caller-owned workspace (torch allocations are 256-byte aligned)."""
@@ -209,6 +224,26 @@ def experts_forward_grouped(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, sc
     _check(moe_experts_forward_grouped(p, x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, sg, su, sd, out,
                                        workspace), "moe_experts_forward_grouped")
     return out
+
+
+def route_problem(T, E, k, method="renormalize", n_group=0, topk_group=0,
+                  routed_scaling_factor=1.0) -> MoeRouteProblem:
+    return MoeRouteProblem(int(T), int(E), int(k), _ROUTE[method] if isinstance(method, str) else int(method),
+                           int(n_group), int(topk_group), float(routed_scaling_factor))
+
+
+def route(logits, k: int, method="renormalize", bias=None, n_group=0, topk_group=0, routed_scaling_factor=1.0,
+          ids=None, weights=None):
+    """moe_route on a float32 [T, E] tensor; returns (ids int32 [T, k], weights float32 [T, k])."""
+    T, E = logits.shape
+    dev = logits.device
+    if ids is None:
+        ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    if weights is None:
+        weights = torch.empty(T, k, dtype=torch.float32, device=dev)
+    p = route_problem(T, E, k, method, n_group, topk_group, routed_scaling_factor)
+    _check(moe_route(p, logits, bias, ids, weights), "moe_route")
+    return ids, weights
 
 
 def align(topk_ids, E: int, workspace=None):

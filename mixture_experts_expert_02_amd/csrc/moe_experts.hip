@@ -18,6 +18,7 @@
 #include "combine.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_skinny.hpp"
+#include "router.hpp"
 
 namespace {
 
@@ -550,6 +551,47 @@ int moe_experts_forward_grouped(const moe_problem* p, const void* x_nvs, const i
   if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
   hipLaunchKernelGGL(moe::k_zero_tail, dim3(p->T), dim3(256), 0, s, (uint16_t*)out_nvs,
                      (const int32_t*)o.status, p->T, p->H);
+  return launch_status();
+}
+
+int moe_route(const moe_route_problem* p, const float* logits, const float* bias, int32_t* topk_ids,
+              float* topk_weights, moe_stream_t stream) {
+  if (!p) return MOE_EINVAL;
+  if (p->T < 0 || p->E <= 0 || p->k <= 0) return MOE_EINVAL;
+  if (p->method != MOE_ROUTE_RENORMALIZE && p->method != MOE_ROUTE_DEEPSEEK_V3) return MOE_EINVAL;
+  if (p->E > moe::kRouteMaxE || p->k > moe::kRouteMaxK) return MOE_ENOTSUP;
+  if (p->k > p->E) return MOE_EINVAL;
+  const bool ds = p->method == MOE_ROUTE_DEEPSEEK_V3;
+  const bool grouped = ds && p->n_group > 1;
+  if (ds) {
+    if (p->n_group < 0 || !std::isfinite(p->routed_scaling_factor)) return MOE_EINVAL;
+    if (grouped && (p->n_group > moe::kRouteMaxGroups || p->E % p->n_group || p->E / p->n_group < 2 ||
+                    p->topk_group < 1 || p->topk_group > p->n_group ||
+                    (long long)p->k > (long long)p->topk_group * (p->E / p->n_group)))
+      return MOE_EINVAL;
+  }
+  if (!logits || !topk_ids || !topk_weights) return MOE_EINVAL;
+  if (((uintptr_t)logits | (uintptr_t)topk_ids | (uintptr_t)topk_weights | (uintptr_t)bias) & 3u) return MOE_EINVAL;
+  if (p->T == 0) return MOE_OK;
+  moe::RouteParams q;
+  q.logits = logits;
+  q.bias = ds ? bias : nullptr;
+  q.T = p->T;
+  q.E = p->E;
+  q.k = p->k;
+  q.method = ds ? 1 : 0;
+  q.n_group = grouped ? p->n_group : 0;
+  q.topk_group = grouped ? p->topk_group : 0;
+  q.scale = ds ? p->routed_scaling_factor : 1.f;
+  q.ids = topk_ids;
+  q.w = topk_weights;
+  const dim3 grid((unsigned)ceil_div(p->T, 4)), block(256);
+  hipStream_t s = (hipStream_t)stream;
+  if (p->E <= 64) hipLaunchKernelGGL(moe::k_route<1>, grid, block, 0, s, q);
+  else if (p->E <= 128) hipLaunchKernelGGL(moe::k_route<2>, grid, block, 0, s, q);
+  else if (p->E <= 256) hipLaunchKernelGGL(moe::k_route<4>, grid, block, 0, s, q);
+  else if (p->E <= 512) hipLaunchKernelGGL(moe::k_route<8>, grid, block, 0, s, q);
+  else hipLaunchKernelGGL(moe::k_route<16>, grid, block, 0, s, q);
   return launch_status();
 }
 

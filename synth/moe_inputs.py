@@ -87,7 +87,7 @@ def workload(name: str, **overrides) -> Workload:
 
 _TAGS = {"x": 1, "logits": 2, "zipf": 3, "w_gate": 4, "w_up": 5, "w_down": 6,
          "s_gate": 7, "s_up": 8, "s_down": 9, "segments": 10, "route_w": 11,
-         "slots": 12}
+         "slots": 12, "router_bias": 13}
 
 
 def seed_for(wl: Workload, tag: str, expert: int = 0, seed: int = 0) -> int:

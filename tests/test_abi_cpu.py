@@ -158,3 +158,37 @@ def test_empty_input_is_a_noop():
     p = B.problem(0, 128, 256, 8, 2)
     assert L.moe_experts_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None, None, fake, fake,
                                  B.moe_experts_workspace_bytes(p), None) == B.MOE_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1, E=8, k=2), B.MOE_EINVAL),
+    (dict(T=4, E=0, k=1), B.MOE_EINVAL),
+    (dict(T=4, E=8, k=0), B.MOE_EINVAL),
+    (dict(T=4, E=8, k=9), B.MOE_EINVAL),
+    (dict(T=4, E=2048, k=2), B.MOE_ENOTSUP),
+    (dict(T=4, E=64, k=33), B.MOE_ENOTSUP),
+    (dict(T=4, E=8, k=2, method=5), B.MOE_EINVAL),
+    (dict(T=4, E=12, k=2, method="deepseek_v3", n_group=5, topk_group=1), B.MOE_EINVAL),   # E % n_group
+    (dict(T=4, E=8, k=2, method="deepseek_v3", n_group=8, topk_group=1), B.MOE_EINVAL),    # one expert per group
+    (dict(T=4, E=16, k=2, method="deepseek_v3", n_group=4, topk_group=0), B.MOE_EINVAL),
+    (dict(T=4, E=16, k=2, method="deepseek_v3", n_group=4, topk_group=5), B.MOE_EINVAL),
+    (dict(T=4, E=16, k=9, method="deepseek_v3", n_group=4, topk_group=2), B.MOE_EINVAL),   # k > kept experts
+    (dict(T=4, E=256, k=8, method="deepseek_v3", n_group=128, topk_group=4), B.MOE_EINVAL),  # > 64 groups
+    (dict(T=4, E=8, k=2, method="deepseek_v3", routed_scaling_factor=math.inf), B.MOE_EINVAL),
+])
+def test_route_invalid_problems_rejected(kw, code):
+    L = B.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    p = B.route_problem(**kw)
+    assert L.moe_route(ctypes.byref(p), fake, None, fake, fake, None) == code
+
+
+def test_route_pointers_and_empty_input():
+    L = B.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    p = B.route_problem(4, 8, 2)
+    for args in ([None, None, fake, fake], [fake, None, None, fake], [fake, None, fake, None],
+                 [odd, None, fake, fake], [fake, odd, fake, fake]):
+        assert L.moe_route(ctypes.byref(p), *args, None) == B.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(B.route_problem(0, 8, 2)), fake, None, fake, fake, None) == B.MOE_OK

@@ -206,3 +206,16 @@ def test_planted_router_mistakes_are_caught(monkeypatch):
     with monkeypatch.context() as m:
         m.setattr(R, "route_deepseek_v3", top1_groups)
         assert _fails(test_deepseek_group_limit_hand_case)
+
+
+def test_deepseek_on_fine_grained_logits_is_well_formed():
+    import synth
+    wl = synth.workload("fine_grained_prefill")
+    l = synth.make_logits(wl, T=512)
+    ids, w = R.route_deepseek_v3(l, 8, bias=synth.make_router_bias(wl), n_group=8, topk_group=4,
+                                 routed_scaling_factor=2.5)
+    G = wl.E // 8
+    for t in range(ids.shape[0]):
+        assert len(set(ids[t].tolist())) == 8
+        assert len({int(e) // G for e in ids[t]}) <= 4
+    np.testing.assert_allclose(w.sum(axis=1), 2.5, rtol=1e-12)

@@ -186,19 +186,29 @@ def expert_matrix(w: Weight, e: int) -> np.ndarray:
 # ----------------------------------------------------------------------------
 def experts_grouped(x_rows: np.ndarray, cu_seqlens: Sequence[int], route_w: np.ndarray,
                     w_gate: Weight, w_up: Weight, w_down: Weight,
-                    act: str = "silu", alpha=1.0, beta=0.0, limit=math.inf) -> np.ndarray:
+                    act: str = "silu", alpha=1.0, beta=0.0, limit=math.inf,
+                    weight_on_input: bool = False) -> np.ndarray:
     """Rows already contiguous per weight row: gate and up grouped GEMMs, the
     activation times the per-row route weight, the down grouped GEMM. Rows past
-    the last end offset come out zero."""
+    the last end offset come out zero.
+
+    weight_on_input: the route weight multiplies the input row before the gate
+    and up GEMMs instead of the activation (moonep_experts page,
+    MoonEPExperts.apply: input-weighted routing is applied to the activations
+    before dispatch, and the experts step then skips its own multiply)."""
     x_rows = np.asarray(x_rows, dtype=np.float64)
     NvS = x_rows.shape[0]
     H = x_rows.shape[1]
+    rw = np.asarray(route_w, dtype=np.float64)[:, None]
+    if weight_on_input:
+        x_rows = x_rows * rw
     gate = grouped_mm(x_rows, lambda g: expert_matrix(w_gate, g), cu_seqlens)
     if gate is None:                                    # every segment empty
         return np.zeros((NvS, H), dtype=np.float64)
     up = grouped_mm(x_rows, lambda g: expert_matrix(w_up, g), cu_seqlens)
     a = activation(act, gate, up, alpha, beta, limit)
-    a = a * np.asarray(route_w, dtype=np.float64)[:, None]
+    if not weight_on_input:
+        a = a * rw
     out = grouped_mm(a, lambda g: expert_matrix(w_down, g), cu_seqlens)
     end = int(cu_seqlens[-1]) if len(cu_seqlens) else 0
     out[end:] = 0.0
@@ -207,7 +217,8 @@ def experts_grouped(x_rows: np.ndarray, cu_seqlens: Sequence[int], route_w: np.n
 
 def experts_forward(x: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
                     w_gate: Weight, w_up: Weight, w_down: Weight,
-                    act: str = "silu", alpha=1.0, beta=0.0, limit=math.inf) -> np.ndarray:
+                    act: str = "silu", alpha=1.0, beta=0.0, limit=math.inf,
+                    weight_on_input: bool = False) -> np.ndarray:
     """Token-major MoE experts layer: group the routed slots by expert, run
     the grouped computation, then combine each token's k slot results in
     ascending j (flashinfer_moe_ep page: route, compute, combine)."""
@@ -219,7 +230,8 @@ def experts_forward(x: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarra
     perm, inv = al["perm"], al["inv_perm"]
     x_rows = x[perm // k]
     rw = np.asarray(topk_weights, dtype=np.float64).reshape(-1)[perm]
-    y = experts_grouped(x_rows, al["cu_seqlens"], rw, w_gate, w_up, w_down, act, alpha, beta, limit)
+    y = experts_grouped(x_rows, al["cu_seqlens"], rw, w_gate, w_up, w_down, act, alpha, beta, limit,
+                        weight_on_input)
     out = np.zeros((T, x.shape[1]), dtype=np.float64)
     for t in range(T):
         acc = np.zeros(x.shape[1], dtype=np.float64)
@@ -232,7 +244,8 @@ def experts_forward(x: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarra
 
 
 def experts_forward_literal(x, topk_ids, topk_weights, w_gate, w_up, w_down,
-                            act="silu", alpha=1.0, beta=0.0, limit=math.inf) -> np.ndarray:
+                            act="silu", alpha=1.0, beta=0.0, limit=math.inf,
+                            weight_on_input=False) -> np.ndarray:
     """The per-token definition: for each token and each of its k slots, run
     the selected expert's MLP on the token, scale by the route weight, and sum
     over the slots in ascending j. Masked (-1) and out-of-range ids add
@@ -249,20 +262,24 @@ def experts_forward_literal(x, topk_ids, topk_weights, w_gate, w_up, w_down,
             e = int(ids[t, j])
             if e < 0 or e >= E:
                 continue
-            g = expert_matrix(w_gate, e) @ x[t]
-            u = expert_matrix(w_up, e) @ x[t]
-            a = activation(act, g, u, alpha, beta, limit) * wts[t, j]
+            xin = x[t] * wts[t, j] if weight_on_input else x[t]
+            g = expert_matrix(w_gate, e) @ xin
+            u = expert_matrix(w_up, e) @ xin
+            a = activation(act, g, u, alpha, beta, limit)
+            if not weight_on_input:
+                a = a * wts[t, j]
             acc = acc + expert_matrix(w_down, e) @ a
         out[t] = acc
     return out
 
 
 def pregrouped_forward(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down,
-                       act="silu", alpha=1.0, beta=0.0, limit=math.inf) -> np.ndarray:
+                       act="silu", alpha=1.0, beta=0.0, limit=math.inf, weight_on_input=False) -> np.ndarray:
     """The pre-grouped entry: rows given in segment order with end offsets and
     per-row route weights (moonep_experts page, MoonEPExperts.apply). Same as
     `experts_grouped`; named for the entry point it checks."""
-    return experts_grouped(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, act, alpha, beta, limit)
+    return experts_grouped(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, act, alpha, beta, limit,
+                           weight_on_input)
 
 
 def _num_experts(w: Weight) -> int:

@@ -422,3 +422,44 @@ def test_swiglu_oai_closed_forms_via_module():
         for u in (-50.0, -3.0, 9.0):
             uc = max(-L, min(L, u))
             assert f(g, u, a, b, L) == pytest.approx(L / (1 + math.exp(-a * L)) * (uc + b), rel=1e-14)
+
+
+# ------------------------------------------------------------------ route weight on the input
+@pytest.mark.parametrize("seed", range(3))
+def test_weight_on_input_top1_is_dense_mlp_of_scaled_input(seed):
+    """Top-1 with the route weight on the input: a dense SwiGLU MLP (torch silu)
+    applied to w * x (moonep_experts page: input-weighted routing scales the
+    activations before dispatch)."""
+    x, _, _, wg, wu, wd = rand_problem(seed, T=5, E=3, k=1)
+    rng = np.random.default_rng(seed + 10)
+    w = rng.uniform(0.1, 2.0, (5, 1)).astype(np.float32)
+    for e in range(3):
+        ids = np.full((5, 1), e, dtype=np.int32)
+        got = oracle.experts_forward(x, ids, w, wg, wu, wd, weight_on_input=True)
+        want = torch_mlp(x * w.astype(np.float64), wg[e], wu[e], wd[e]).numpy()
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+        # differs from the output-side weighting (silu is not homogeneous)
+        other = oracle.experts_forward(x, ids, w, wg, wu, wd)
+        assert not np.allclose(got, other, rtol=1e-3)
+
+
+def test_weight_on_input_grouped_equals_literal():
+    x, ids, w, wg, wu, wd = rand_problem(4, T=7, E=4, k=2)
+    for act, kw in (("silu", {}), ("situ", dict(alpha=1.5, beta=0.8))):
+        a = oracle.experts_forward(x, ids, w, wg, wu, wd, act=act, weight_on_input=True, **kw)
+        b = oracle.experts_forward_literal(x, ids, w, wg, wu, wd, act=act, weight_on_input=True, **kw)
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def test_situ_forward_top1_is_dense_situ_mlp():
+    """SiTu through the whole forward equals a dense MLP written with torch's
+    tanh and sigmoid from the page's formula: alpha*tanh(g/alpha)*sigmoid(g)
+    times beta*tanh(u/beta)."""
+    x, _, _, wg, wu, wd = rand_problem(2, T=4, E=2, k=1)
+    al, be = 1.7, 0.6
+    ids = np.ones((4, 1), dtype=np.int32)
+    got = oracle.experts_forward(x, ids, np.ones((4, 1), np.float32), wg, wu, wd, act="situ", alpha=al, beta=be)
+    X, G, U, D = (torch.as_tensor(np.asarray(v, dtype=np.float64)) for v in (x, wg[1], wu[1], wd[1]))
+    g, u = X @ G.T, X @ U.T
+    want = ((al * torch.tanh(g / al) * torch.sigmoid(g)) * (be * torch.tanh(u / be))) @ D.T
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)

@@ -73,8 +73,10 @@ typedef enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1 } moe_wfmt;
 /* Activation. moonep_experts page, module docstring (silu(gate) * up);
  * trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsBase (SwiGLU-OAI with alpha, beta,
  * clamp limit). SwiGLU-OAI is read as
- *   g' = min(g, limit), u' = clamp(u, -limit, limit), f = g' * sigmoid(alpha g') * (u' + beta). */
-typedef enum { MOE_ACT_SILU = 0, MOE_ACT_SWIGLU_OAI = 1 } moe_act;
+ *   g' = min(g, limit), u' = clamp(u, -limit, limit), f = g' * sigmoid(alpha g') * (u' + beta).
+ * SiTu, as the same class's constructor comment gives it:
+ *   f = alpha * tanh(g / alpha) * sigmoid(g) * beta * tanh(u / beta), alpha > 0, beta > 0. */
+typedef enum { MOE_ACT_SILU = 0, MOE_ACT_SWIGLU_OAI = 1, MOE_ACT_SITU = 2 } moe_act;
 
 typedef struct {
   int32_t T;     /* tokens: rows of x and out (NvS for the pre-grouped entry) */
@@ -84,9 +86,15 @@ typedef struct {
   int32_t k;     /* slots per token (ignored by the pre-grouped entry) */
   int32_t wfmt;  /* moe_wfmt */
   int32_t act;   /* moe_act */
-  float alpha;   /* SwiGLU-OAI only */
-  float beta;    /* SwiGLU-OAI only */
+  float alpha;   /* SwiGLU-OAI and SiTu */
+  float beta;    /* SwiGLU-OAI and SiTu */
   float limit;   /* SwiGLU-OAI only; > 0, may be +inf */
+  int32_t weight_on_input; /* 0: route weight multiplies the activation (default);
+                              1: it multiplies the token's input row before GEMM1 (each
+                              routed row x * w rounded to bf16) and the activation is
+                              not weighted (moonep_experts page, MoonEPExperts.apply,
+                              input-weighted top-1 routing). Costs one more read and
+                              write of the routed rows. */
 } moe_problem;
 
 /* Byte offsets of the intermediates inside a forward workspace (for tests and

@@ -18,9 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libmoe_experts.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_W_BF16, MOE_W_MXFP4 = 0, 1
-MOE_ACT_SILU, MOE_ACT_SWIGLU_OAI = 0, 1
+MOE_ACT_SILU, MOE_ACT_SWIGLU_OAI, MOE_ACT_SITU = 0, 1, 2
 
-_ACT = {"silu": MOE_ACT_SILU, "swiglu_oai": MOE_ACT_SWIGLU_OAI}
+_ACT = {"silu": MOE_ACT_SILU, "swiglu_oai": MOE_ACT_SWIGLU_OAI, "situ": MOE_ACT_SITU}
 _WFMT = {"bf16": MOE_W_BF16, "mxfp4": MOE_W_MXFP4}
 
 EXPORTED = (
@@ -37,7 +37,7 @@ class MoeProblem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("wfmt", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
-                ("limit", ctypes.c_float)]
+                ("limit", ctypes.c_float), ("weight_on_input", ctypes.c_int32)]
 
 
 class MoeRouteProblem(ctypes.Structure):
@@ -100,9 +100,11 @@ def strerror(status: int) -> str:
     return lib().moe_strerror(status).decode()
 
 
-def problem(T, H, I, E, k=1, wfmt="bf16", act="silu", alpha=1.0, beta=0.0, limit=math.inf) -> MoeProblem:
+def problem(T, H, I, E, k=1, wfmt="bf16", act="silu", alpha=1.0, beta=0.0, limit=math.inf,
+            weight_on_input=False) -> MoeProblem:
     return MoeProblem(int(T), int(H), int(I), int(E), int(k), _WFMT[wfmt] if isinstance(wfmt, str) else int(wfmt),
-                      _ACT[act] if isinstance(act, str) else int(act), float(alpha), float(beta), float(limit))
+                      _ACT[act] if isinstance(act, str) else int(act), float(alpha), float(beta), float(limit),
+                      int(weight_on_input))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -191,14 +193,14 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def experts_forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, scales=None, act="silu", alpha=1.0, beta=0.0,
-                    limit=math.inf, out=None, workspace=None) -> torch.Tensor:
+                    limit=math.inf, out=None, workspace=None, weight_on_input=False) -> torch.Tensor:
     """Token-major experts step on torch tensors; allocates out/workspace if not given."""
     T, H = x.shape
     k = topk_ids.shape[1]
     E = w_gate.shape[0]
     wfmt = "mxfp4" if w_gate.dtype == torch.uint8 else "bf16"
     I = w_gate.shape[1]
-    p = problem(T, H, I, E, k, wfmt, act, alpha, beta, limit)
+    p = problem(T, H, I, E, k, wfmt, act, alpha, beta, limit, weight_on_input)
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
     if workspace is None:
@@ -210,12 +212,12 @@ def experts_forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, scales=None
 
 
 def experts_forward_grouped(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, scales=None, act="silu", alpha=1.0,
-                            beta=0.0, limit=math.inf, out=None, workspace=None) -> torch.Tensor:
+                            beta=0.0, limit=math.inf, out=None, workspace=None, weight_on_input=False) -> torch.Tensor:
     NvS, H = x_nvs.shape
     G = w_gate.shape[0]
     I = w_gate.shape[1]
     wfmt = "mxfp4" if w_gate.dtype == torch.uint8 else "bf16"
-    p = problem(NvS, H, I, G, 1, wfmt, act, alpha, beta, limit)
+    p = problem(NvS, H, I, G, 1, wfmt, act, alpha, beta, limit, weight_on_input)
     if out is None:
         out = torch.empty(NvS, H, dtype=torch.bfloat16, device=x_nvs.device)
     if workspace is None:

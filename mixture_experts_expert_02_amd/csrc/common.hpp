@@ -42,6 +42,7 @@ __device__ __forceinline__ float sigmoidf_fast(float x) {
 //   act 1: SwiGLU-OAI, g' = min(g, limit), u' = clamp(u, -limit, limit),
 //          g' * sigmoid(alpha g') * (u' + beta)   (trtllm_mxfp4_moe page,
 //          TrtLlmMxfp4ExpertsBase parameters; formula is the gpt-oss reading)
+//   act 2: SiTu, alpha tanh(g / alpha) sigmoid(g) * beta tanh(u / beta)
 struct ActParams {
   int32_t kind;
   float alpha, beta, limit;
@@ -49,6 +50,8 @@ struct ActParams {
 
 __device__ __forceinline__ float gated_act(const ActParams& a, float g, float u) {
   if (a.kind == 0) return g * sigmoidf_fast(g) * u;
+  if (a.kind == 2)  // SiTu (trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsBase constructor comment)
+    return a.alpha * tanhf(g / a.alpha) * sigmoidf_fast(g) * (a.beta * tanhf(u / a.beta));
   g = fminf(g, a.limit);
   u = fminf(fmaxf(u, -a.limit), a.limit);
   return g * sigmoidf_fast(a.alpha * g) * (u + a.beta);

@@ -60,7 +60,7 @@ struct Params {
   int32_t ncu;             // compute units of the device (one block each)
   int64_t c_split;         // elements between the partial outputs of consecutive K ranges
   uint16_t* C;             // [rows, N] bf16 output, sorted row order (GEMM2 split: [S, rows, N])
-  const float* row_w;      // GEMM1: route weight per sorted row
+  const float* row_w;      // GEMM1: route weight per sorted row, or nullptr (weight already on the input)
   ActParams act;
 };
 
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
         if (GATED) {
 #pragma unroll
           for (int r3 = 0; r3 < 4; ++r3)
-            if (rbase + r3 < wrows) w4[r3] = p.row_w[wrow0 + rbase + r3];
+            if (p.row_w && rbase + r3 < wrows) w4[r3] = p.row_w[wrow0 + rbase + r3];
         }
 #pragma unroll
         for (int r3 = 0; r3 < 4; ++r3) {

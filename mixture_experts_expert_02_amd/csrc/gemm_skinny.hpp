@@ -101,7 +101,7 @@ struct Params {
   int32_t mt_cap;
   int32_t n_tiles;        // ceil(N / block_cols)
   uint16_t* C;
-  const float* row_w;
+  const float* row_w;     // route weight per sorted row, or nullptr (weight already on the input)
   ActParams act;
 };
 
@@ -468,7 +468,8 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
     if (row >= rows) continue;
     uint16_t* dst = p.C + (size_t)(row0 + row) * N;
     if (GATED) {
-      if (c0 < N) dst[c0] = f32_to_bf16_rne(gated_act(p.act, acc0[r], acc1[r]) * p.row_w[row0 + row]);
+      if (c0 < N)
+        dst[c0] = f32_to_bf16_rne(gated_act(p.act, acc0[r], acc1[r]) * (p.row_w ? p.row_w[row0 + row] : 1.f));
     } else {
       if (c0 < N) dst[c0] = f32_to_bf16_rne(acc0[r]);
       if (c1 < N) dst[c1] = f32_to_bf16_rne(acc1[r]);

@@ -19,6 +19,7 @@
 #include "gemm_bf16.hpp"
 #include "gemm_skinny.hpp"
 #include "router.hpp"
+#include "scale_rows.hpp"
 
 namespace {
 
@@ -54,7 +55,7 @@ struct Plan {
   bool fused_align;
   int chunk, nch;
   // byte offsets
-  size_t status, counts, cu, offsets, tile_seg, tile_row0, blkcnt, blkbad, perm, inv_perm, w_sorted, act,
+  size_t status, counts, cu, offsets, tile_seg, tile_row0, blkcnt, blkbad, perm, inv_perm, w_sorted, xs, act,
       xq, aq, y, total;
 };
 
@@ -63,11 +64,16 @@ int check_problem(const moe_problem* p, bool grouped) {
   if (p->T < 0 || p->H <= 0 || p->I <= 0 || p->E <= 0) return MOE_EINVAL;
   if (!grouped && (p->k <= 0 || p->k > p->E)) return MOE_EINVAL;
   if (p->wfmt != MOE_W_BF16 && p->wfmt != MOE_W_MXFP4) return MOE_EINVAL;
-  if (p->act != MOE_ACT_SILU && p->act != MOE_ACT_SWIGLU_OAI) return MOE_EINVAL;
+  if (p->act != MOE_ACT_SILU && p->act != MOE_ACT_SWIGLU_OAI && p->act != MOE_ACT_SITU) return MOE_EINVAL;
   if (p->act == MOE_ACT_SWIGLU_OAI) {
     if (!std::isfinite(p->alpha) || !std::isfinite(p->beta) || std::isnan(p->limit)) return MOE_EINVAL;
     if (!(p->limit > 0.f)) return MOE_ENOTSUP;
   }
+  if (p->act == MOE_ACT_SITU) {  // the page requires both parameters > 0
+    if (!std::isfinite(p->alpha) || !std::isfinite(p->beta)) return MOE_EINVAL;
+    if (!(p->alpha > 0.f) || !(p->beta > 0.f)) return MOE_ENOTSUP;
+  }
+  if (p->weight_on_input != 0 && p->weight_on_input != 1) return MOE_EINVAL;
   if (p->H % 64 || p->I % 64) return MOE_ENOTSUP;
   if (p->wfmt == MOE_W_MXFP4 && (p->H > moe::skinny::kMaxMxfp4K || p->I > moe::skinny::kMaxMxfp4K))
     return MOE_ENOTSUP;
@@ -135,6 +141,7 @@ Plan make_plan(const moe_problem& p, bool grouped, size_t ws_bytes = ~(size_t)0)
     pl.inv_perm = take(4ull * pl.M);
     pl.w_sorted = take(4ull * pl.M);
   }
+  if (p.weight_on_input) pl.xs = take(2ull * pl.M * p.H);  // routed rows x * w, sorted order
   pl.act = take(2ull * pl.M * p.I);
   if (p.wfmt == MOE_W_MXFP4) {  // activation rows split for the block-scaled MFMA, sorted order
     pl.xq = take(quant_bytes(pl.M, p.H));
@@ -399,12 +406,24 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
 
   const bool mx = p->wfmt == MOE_W_MXFP4;
   GemmIO g1{x, o.perm, p->k, wg, wu, sg, su, p->I, p->H, at<void>(ws, pl.act), o.w_sorted, 1, 0, {}};
+  if (p->weight_on_input) {  // rows x * w in sorted order; no weight in GEMM1's epilogue
+    g1.A = at<void>(ws, pl.xs);
+    g1.a_perm = nullptr;
+    g1.row_w = nullptr;
+  }
   if (mx) {  // x split in sorted row order: GEMM1 reads its rows without the permutation
     g1.Aq = quant_rows_at(ws, pl.xq, pl.M, p->H);
     g1.a_perm = nullptr;
   }
   mark(1);
-  if (mx) launch_quant(x, pl.M, p->H, g1.Aq, s, o.perm, p->k, o.status);
+  if (p->weight_on_input)
+    hipLaunchKernelGGL(moe::k_scale_rows, dim3((unsigned)pl.M), dim3(256), 0, s, (const uint16_t*)x,
+                       (const int32_t*)o.perm, p->k, (const float*)o.w_sorted, (const int32_t*)o.status, M, p->H,
+                       at<uint16_t>(ws, pl.xs));
+  if (mx) {
+    if (p->weight_on_input) launch_quant(g1.A, pl.M, p->H, g1.Aq, s);
+    else launch_quant(x, pl.M, p->H, g1.Aq, s, o.perm, p->k, o.status);
+  }
   if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
 
   const long long y_split = pl.M * p->H;
@@ -538,9 +557,16 @@ int moe_experts_forward_grouped(const moe_problem* p, const void* x_nvs, const i
   if ((rc = launch_status())) return rc;
   const bool mx = p->wfmt == MOE_W_MXFP4;
   GemmIO g1{x_nvs, nullptr, 1, w_gate, w_up, s_gate, s_up, p->I, p->H, at<void>(ws, pl.act), route_w, 1, 0, {}};
+  if (p->weight_on_input) {
+    g1.A = at<void>(ws, pl.xs);
+    g1.row_w = nullptr;
+    hipLaunchKernelGGL(moe::k_scale_rows, dim3((unsigned)p->T), dim3(256), 0, s, (const uint16_t*)x_nvs,
+                       (const int32_t*)nullptr, 1, route_w, (const int32_t*)nullptr, p->T, p->H,
+                       at<uint16_t>(ws, pl.xs));
+  }
   if (mx) {
     g1.Aq = quant_rows_at(ws, pl.xq, pl.M, p->H);
-    launch_quant(x_nvs, pl.M, p->H, g1.Aq, s);
+    launch_quant(g1.A, pl.M, p->H, g1.Aq, s);
   }
   if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
   GemmIO g2{at<void>(ws, pl.act), nullptr, 1, w_down, nullptr, s_down, nullptr, p->H, p->I, out_nvs, nullptr, 1, 0, {}};

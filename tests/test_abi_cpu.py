@@ -83,6 +83,11 @@ def test_workspace_room_for_split_down_projection(monkeypatch):
     (dict(T=1 << 20, H=2048, I=256), B.MOE_ENOTSUP),  # T*H = 2^31: beyond 32-bit row offsets
     (dict(T=1 << 18, k=2, H=128, I=4096), B.MOE_ENOTSUP),  # rows*I = 2^31
     (dict(H=32768, I=32832), B.MOE_ENOTSUP),      # one expert's I*H above 2^30
+    (dict(act="situ", alpha=0.0, beta=1.0), B.MOE_ENOTSUP),   # SiTu needs alpha > 0 and beta > 0
+    (dict(act="situ", alpha=1.0, beta=-1.0), B.MOE_ENOTSUP),
+    (dict(act="situ", alpha=math.inf, beta=1.0), B.MOE_EINVAL),
+    (dict(act=3), B.MOE_EINVAL),
+    (dict(weight_on_input=2), B.MOE_EINVAL),
 ])
 def test_invalid_problems_rejected(kw, code):
     base = dict(T=16, H=128, I=256, E=8, k=2)
@@ -192,3 +197,12 @@ def test_route_pointers_and_empty_input():
                  [odd, None, fake, fake], [fake, odd, fake, fake]):
         assert L.moe_route(ctypes.byref(p), *args, None) == B.MOE_EINVAL
     assert L.moe_route(ctypes.byref(B.route_problem(0, 8, 2)), fake, None, fake, fake, None) == B.MOE_OK
+
+
+def test_weight_on_input_workspace_holds_scaled_rows():
+    p0 = B.problem(64, 128, 256, 8, 2)
+    p1 = B.problem(64, 128, 256, 8, 2, weight_on_input=True)
+    assert B.moe_experts_workspace_bytes(p1) >= B.moe_experts_workspace_bytes(p0) + 64 * 2 * 128 * 2
+    g0 = B.problem(100, 128, 256, 5)
+    g1 = B.problem(100, 128, 256, 5, weight_on_input=True)
+    assert B.moe_experts_grouped_workspace_bytes(g1) >= B.moe_experts_grouped_workspace_bytes(g0) + 100 * 128 * 2

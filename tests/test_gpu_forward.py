@@ -75,17 +75,28 @@ CASES = [
     ("decode_mxfp4_ktail", (6, 2880, 192, 4, 2), "mxfp4", "swiglu_oai", {}),   # 90 scale blocks: ragged K steps
     ("mxfp4_many_rows", (150, 128, 256, 3, 2), "mxfp4", "silu", {}),          # several 16-row tiles per expert
     ("single_token", (1, 128, 256, 8, 2), "bf16", "silu", {}),
+    ("prefill_situ", (520, 128, 256, 4, 2), "bf16", "situ", {}),
+    ("decode_bf16_situ", (9, 128, 320, 12, 4), "bf16", "situ", {}),
+    ("decode_mxfp4_situ", (9, 256, 320, 6, 3), "mxfp4", "situ", {}),
+    ("prefill_weight_on_input_top1", (700, 256, 384, 5, 1), "bf16", "silu", {"on_input": True}),
+    ("prefill_weight_on_input_k2_masked", (600, 128, 256, 4, 2), "bf16", "swiglu_oai",
+     {"on_input": True, "masked": 0.1}),
+    ("decode_mxfp4_weight_on_input", (13, 192, 128, 5, 1), "mxfp4", "silu", {"on_input": True}),
+    ("decode_bf16_weight_on_input", (20, 256, 192, 16, 1), "bf16", "situ", {"on_input": True}),
 ]
+ACT_PARAMS = {"silu": {}, "swiglu_oai": dict(alpha=1.702, beta=1.0, limit=7.0), "situ": dict(alpha=1.5, beta=0.8)}
 
 
 @pytest.mark.parametrize("name,shape,wfmt,act,extra", CASES, ids=[c[0] for c in CASES])
 def test_forward_matches_oracle(name, shape, wfmt, act, extra):
     T, H, I, E, k = shape
     print(f"[forward] {name} T={T} H={H} I={I} E={E} k={k} {wfmt} {act}", flush=True)
+    extra = dict(extra)
+    on_input = extra.pop("on_input", False)
     x, ids, w, W, S = make_problem(zlib.crc32(name.encode()) % 1000, T, H, I, E, k, wfmt, **extra)
-    act_kw = dict(act=act)
-    if act == "swiglu_oai":
-        act_kw.update(alpha=1.702, beta=1.0, limit=7.0)
+    act_kw = dict(act=act, **ACT_PARAMS[act])
+    if on_input:
+        act_kw["weight_on_input"] = True
     out = run_gpu(x, ids, w, W, S, act_kw)
     ref = oracle_out(x, ids, w, W, S, act_kw)
     got = to_np(out)
@@ -204,22 +215,24 @@ def grouped_case(seed, lengths, tail, H=256, I=384, wfmt="bf16"):
     return x, cu, rw, W, S
 
 
-@pytest.mark.parametrize("lengths,tail,wfmt", [
-    ([300, 0, 257, 1, 0, 512, 40], 13, "bf16"),     # empty segments, ragged, padding rows
-    ([0, 0, 5, 0], 7, "bf16"),                      # decode-sized (weight-streaming path)
-    ([33, 0, 70, 2], 5, "mxfp4"),
-    ([600, 600], 0, "bf16"),
+@pytest.mark.parametrize("lengths,tail,wfmt,on_input", [
+    ([300, 0, 257, 1, 0, 512, 40], 13, "bf16", False),     # empty segments, ragged, padding rows
+    ([0, 0, 5, 0], 7, "bf16", False),                      # decode-sized (weight-streaming path)
+    ([33, 0, 70, 2], 5, "mxfp4", False),
+    ([600, 600], 0, "bf16", False),
+    ([300, 0, 257, 1, 0, 512, 40], 13, "bf16", True),      # route weight on the input rows
+    ([33, 0, 70, 2], 5, "mxfp4", True),
 ])
-def test_grouped_matches_oracle(lengths, tail, wfmt):
+def test_grouped_matches_oracle(lengths, tail, wfmt, on_input):
     x, cu, rw, W, S = grouped_case(len(lengths) * 10 + tail, lengths, tail, wfmt=wfmt)
-    print(f"[grouped] lengths={lengths} tail={tail} {wfmt}", flush=True)
+    print(f"[grouped] lengths={lengths} tail={tail} {wfmt} on_input={on_input}", flush=True)
     Wd = [t.to(DEV) for t in W]
     Sd = None if S is None else [t.to(DEV) for t in S]
     out = B.experts_forward_grouped(x.to(DEV), torch.from_numpy(cu).to(DEV), torch.from_numpy(rw).to(DEV), *Wd,
-                                    scales=Sd)
+                                    scales=Sd, weight_on_input=on_input)
     torch.cuda.synchronize()
     Wn = [to_np(t) for t in W] if S is None else [(c.numpy(), s.numpy()) for c, s in zip(W, S)]
-    ref = oracle.pregrouped_forward(to_np(x), cu, rw, *Wn)
+    ref = oracle.pregrouped_forward(to_np(x), cu, rw, *Wn, weight_on_input=on_input)
     got = to_np(out)
     assert rel_err(got, ref) <= TOL
     assert np.all(got[int(cu[-1]):] == 0)

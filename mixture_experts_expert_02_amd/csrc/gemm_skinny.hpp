@@ -356,13 +356,17 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
   // Chunks past the last are loaded too (the loop below has no exits); their
   // offset is moved past the segment, where buffer loads return 0 without a
   // memory access.
+  // MXFP4: a lane's 16 bytes of the last chunk that lie past its row end
+  // are not read either (their offset is moved past the segment too); the
+  // next row's bytes would only meet zero activations.
   auto load_chunk = [&](WSet<FMT>& w, int c) {
     const int so = c < nch ? c * C::SPC * 4 * BLOCK_BYTES : (int)segbytes;
+    const bool in_row = (uint32_t)so + 16u * l16 < rowbytes;
 #pragma unroll
     for (int u = 0; u < C::SPC; ++u) {
       if (FMT == W_MXFP4) {  // w.w0[u]: instruction u (rows 4 u + q)
-        w.w0[u].q[0] = __builtin_amdgcn_raw_buffer_load_b128(rs0, vo0[u], so, 0);
-        w.w1[u].q[0] = __builtin_amdgcn_raw_buffer_load_b128(rs1, vo1[u], so, 0);
+        w.w0[u].q[0] = __builtin_amdgcn_raw_buffer_load_b128(rs0, in_row ? vo0[u] : segbytes, so, 0);
+        w.w1[u].q[0] = __builtin_amdgcn_raw_buffer_load_b128(rs1, in_row ? vo1[u] : segbytes, so, 0);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

@@ -207,12 +207,20 @@ __global__ __launch_bounds__(1024) void k_align_scan(int32_t* blkcnt, const int3
   int32_t* mts = off + E;      // [E]
   int32_t* scratch = mts + E;  // [32]
   const int tid = threadIdx.x;
+  // per expert, an exclusive scan over the chunks; the counts are read eight
+  // chunks at a time so that the loads overlap
   for (int e = tid; e < E; e += 1024) {
     int run = 0;
-    for (int c = 0; c < nch; ++c) {
-      const int v = blkcnt[(size_t)c * E + e];
-      blkcnt[(size_t)c * E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < nch; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = c0 + u < nch ? blkcnt[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < nch) {
+          blkcnt[(size_t)(c0 + u) * E + e] = run;
+          run += v[u];
+        }
     }
     cnt[e] = run;
     off[e] = run;

@@ -23,24 +23,36 @@ struct SplitSum {
 };
 
 // One workgroup per token; each thread sums 8 consecutive columns, slot j
-// outer and K range s inner, both ascending.
+// outer and K range s inner, both ascending. The (j, s) rows are fetched
+// eight at a time before any is added, so a thread has up to eight loads in
+// flight instead of one; the additions keep the order above.
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* y, const int32_t* inv_perm, int T, int k,
                                                  int H, const SplitSum ss, uint16_t* out) {
   const int t = blockIdx.x;
   if (t >= T) return;
   const int S = ss.s_cap > 1 ? split_k_count(ss.status[2] * ss.n_tiles, ss.kt, ss.ncu, ss.s_cap) : 1;
+  const int n = k * S;  // (j, s) pairs, j-major
+  const int32_t* ip = inv_perm + (size_t)t * k;
   for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int p = inv_perm[(size_t)t * k + j];
-      if (p < 0) continue;
-      for (int sp = 0; sp < S; ++sp) {
-        const u32x4 v = *(const u32x4*)(y + (size_t)sp * ss.stride + (size_t)p * H + h);
-        const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+    for (int base = 0; base < n; base += 8) {
+      u32x4 v[8];
+      bool ok[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = base + u;
+        const int j = idx / S, sp = idx - j * S;
+        const int p = idx < n ? ip[j] : -1;
+        ok[u] = p >= 0;
+        if (ok[u]) v[u] = *(const u32x4*)(y + (size_t)sp * ss.stride + (size_t)p * H + h);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (!ok[u]) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += bf16_bits_to_f32(w[i] & 0xffffu);
-          acc[2 * i + 1] += bf16_bits_to_f32(w[i] >> 16);
+          acc[2 * i] += bf16_bits_to_f32(v[u][i] & 0xffffu);
+          acc[2 * i + 1] += bf16_bits_to_f32(v[u][i] >> 16);
         }
       }
     }

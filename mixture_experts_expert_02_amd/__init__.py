@@ -8,5 +8,5 @@ from .binding import (  # noqa: F401
     MoeError, align, experts_forward, experts_forward_grouped, moe_align, moe_align_workspace_bytes,
     moe_device_error, moe_experts_forward, moe_experts_forward_grouped, moe_experts_forward_timed,
     moe_experts_grouped_workspace_bytes, moe_experts_workspace_bytes, moe_experts_workspace_layout,
-    moe_strerror, problem,
+    moe_route, moe_strerror, problem, route, route_problem,
 )

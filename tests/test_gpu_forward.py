@@ -83,6 +83,10 @@ CASES = [
      {"on_input": True, "masked": 0.1}),
     ("decode_mxfp4_weight_on_input", (13, 192, 128, 5, 1), "mxfp4", "silu", {"on_input": True}),
     ("decode_bf16_weight_on_input", (20, 256, 192, 16, 1), "bf16", "situ", {"on_input": True}),
+    # MXFP4 scale staging with 8 and 16 pieces per thread (K above 4096 and 8192, up to the 16384 limit)
+    ("decode_mxfp4_k8192", (4, 8192, 256, 3, 2), "mxfp4", "swiglu_oai", {}),
+    ("decode_mxfp4_k16384", (3, 256, 16384, 2, 1), "mxfp4", "silu", {}),
+    ("decode_mxfp4_k6144_ragged", (5, 6144, 320, 3, 2), "mxfp4", "silu", {}),
 ]
 ACT_PARAMS = {"silu": {}, "swiglu_oai": dict(alpha=1.702, beta=1.0, limit=7.0), "situ": dict(alpha=1.5, beta=0.8)}
 

@@ -114,7 +114,8 @@ def grouped_mm(a: np.ndarray, w_of: Callable[[int], np.ndarray], cu_seqlens: Seq
 def silu(g):
     """silu(g) = g * sigmoid(g) (moonep_experts page, module docstring)."""
     g = np.asarray(g, dtype=np.float64)
-    return g / (1.0 + np.exp(-g))
+    with np.errstate(over="ignore"):  # exp(-g) = inf for very negative g gives the limit 0
+        return g / (1.0 + np.exp(-g))
 
 
 def swiglu_oai(g, u, alpha: float, beta: float, limit: float):
@@ -125,7 +126,8 @@ def swiglu_oai(g, u, alpha: float, beta: float, limit: float):
     f = g' * sigmoid(alpha * g') * (u' + beta)."""
     g = np.minimum(np.asarray(g, dtype=np.float64), limit)
     u = np.clip(np.asarray(u, dtype=np.float64), -limit, limit)
-    return g / (1.0 + np.exp(-alpha * g)) * (u + beta)
+    with np.errstate(over="ignore"):  # exp overflow to inf gives the limit 0
+        return g / (1.0 + np.exp(-alpha * g)) * (u + beta)
 
 
 def situ(g, u, alpha: float, beta: float):
@@ -134,7 +136,8 @@ def situ(g, u, alpha: float, beta: float):
     right = beta*tanh(u/beta) on the up projection, product of the two."""
     g = np.asarray(g, dtype=np.float64)
     u = np.asarray(u, dtype=np.float64)
-    return alpha * np.tanh(g / alpha) / (1.0 + np.exp(-g)) * (beta * np.tanh(u / beta))
+    with np.errstate(over="ignore"):  # exp overflow to inf gives the limit 0
+        return alpha * np.tanh(g / alpha) / (1.0 + np.exp(-g)) * (beta * np.tanh(u / beta))
 
 
 def activation(name: str, g, u, alpha=1.0, beta=0.0, limit=math.inf):

@@ -74,7 +74,8 @@ def route_renormalize(logits: np.ndarray, k: int):
 
 def _sigmoid_f32(l: np.ndarray) -> np.ndarray:
     """sigmoid in float64, rounded to float32 (the scores decisions are taken on)."""
-    return (1.0 / (1.0 + np.exp(-l))).astype(np.float32)
+    with np.errstate(over="ignore"):  # exp overflow to inf gives the limit 0
+        return (1.0 / (1.0 + np.exp(-l))).astype(np.float32)
 
 
 def route_deepseek_v3(logits: np.ndarray, k: int, bias: np.ndarray | None = None, n_group: int = 0,

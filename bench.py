@@ -6,7 +6,10 @@ line. Default workload: the Mixtral-shaped prefill layer (T=4096, H=4096,
 I=14336, E=8, top-2, bf16), reported in TFLOP/s of routed-row GEMM work.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--calib-copy]
+                  [--no-cpu-baseline] [--calib-copy] [--router]
+
+--workload pregrouped times the pre-grouped entry (segments already
+contiguous, caller's cu_seqlens) instead of the token-major step.
 
 Per-kernel times come from hipEvents that the library records between its
 launches on the benchmark's stream (moe_experts_forward_timed), over the same
@@ -33,7 +36,9 @@ METRIC = "MoE experts TFLOP/s (bf16 prefill) + weight-stream GB/s (MXFP4 decode)
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 200 for the MXFP4 decode workload, whose step is 0.25 ms, "
+                         "so that the timed region's fixed start and end cost stays small per step)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -170,6 +175,101 @@ def cpu_baseline(wl, x, ids, w, W, S, n_tokens):
                       f"{dt:.1f} s"}
 
 
+def cpu_baseline_pregrouped(wl, x, cu, rw, W, n_rows):
+    """The float64 oracle on rows [0, n_rows) of the pre-grouped layout (the
+    segments they fall in, with their weights copied to the host)."""
+    import numpy as np
+    import threadpoolctl
+    import torch
+    import oracle
+    import synth
+    segs = [g for g in range(len(cu)) if (cu[g - 1] if g else 0) < n_rows and cu[g] > (cu[g - 1] if g else 0)]
+    sub_cu = np.minimum(np.array([cu[g] for g in segs]), n_rows)
+    xs = synth.bf16_to_f32(x[:n_rows])
+    sel = torch.as_tensor(segs, device=x.device)
+    Wh = [synth.bf16_to_f32(t.index_select(0, sel)) for t in W]
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    oracle.pregrouped_forward(xs, sub_cu, rw[:n_rows], *Wh)
+    dt = time.perf_counter() - t0
+    flops = 6.0 * n_rows * wl.H * wl.I
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n_rows} of {wl.T} rows ({len(segs)} segments) of {wl.name}, float64 numpy, {dt:.1f} s"}
+
+
+def bench_pregrouped(args, wl, dev):
+    """The pre-grouped entry (rows already contiguous per weight row, caller's
+    cu_seqlens) on the pre-grouped workload: GEMM1, GEMM2 and the zero tail."""
+    import numpy as np
+    import torch
+    import synth
+    from mixture_experts_expert_02_amd import binding as B
+    print(f"[bench] workload {wl.name}: NvS={wl.T} H={wl.H} I={wl.I} segments={wl.E}", file=sys.stderr, flush=True)
+    lengths, source = synth.make_pregrouped_layout(wl)
+    cu = np.cumsum(lengths).astype(np.int32)
+    x = synth.make_x(wl, device=dev)
+    W = synth.make_bf16_weights(wl, device=dev, source=source)
+    rw = synth.make_route_weights_nvs(wl)
+    cu_d, rw_d = torch.from_numpy(cu).to(dev), torch.from_numpy(rw).to(dev)
+    p = B.problem(wl.T, wl.H, wl.I, wl.E, 1, wl.wfmt, wl.act, wl.alpha, wl.beta, wl.limit)
+    ws = B.alloc_workspace(B.moe_experts_grouped_workspace_bytes(p), dev)
+    out = torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    hev = HipEvents()
+
+    def step(evs=()):
+        rc = B.moe_experts_forward_grouped_timed(p, x, cu_d, rw_d, *W, None, None, None, out, ws, list(evs),
+                                                 stream=stream)
+        if rc != 0:
+            raise B.MoeError(rc, "moe_experts_forward_grouped_timed")
+
+    for _ in range(args.warmup):
+        step()
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        del a, b
+    torch.cuda.synchronize()
+    K = args.steps if args.steps is not None else 20
+    evs = [hev.create(5) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = ("prep", "gemm1", "gemm2", "zero_tail")
+    avg = {s: float(np.mean([hev.elapsed_ms(e[j], e[j + 1]) for e in evs])) for j, s in enumerate(stages)}
+    step_ms = float(np.mean([hev.elapsed_ms(e[0], e[4]) for e in evs]))
+    for e in evs:
+        hev.destroy(e)
+    ms_per_step = wall * 1e3 / K
+    M = int(cu[-1])
+    n_touched = int(np.sum(lengths > 0))
+    value = 6.0 * M * wl.H * wl.I / (ms_per_step * 1e-3) / 1e12
+    achieved = 4.0 * M * wl.H * wl.I / (avg["gemm1"] * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": counter_traffic(wl.name, wl.wfmt),
+            "kernel": "gemm1 (gate+up, bf16)",
+            "algorithmic_bytes": n_touched * 2 * wl.I * wl.H * 2 + M * wl.H * 2 + M * wl.I * 2}
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "NvS": wl.T, "H": wl.H, "I": wl.I, "segments": wl.E, "weights": wl.wfmt,
+                   "activation": wl.act, "routed_rows": M, "touched_experts": n_touched},
+        "stage_ms": {s: round(v, 4) for s, v in avg.items()},
+        "event_ms_per_step": round(step_ms, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_pregrouped(wl, x, cu, rw, W, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.print_source_hash:
@@ -189,7 +289,7 @@ def main():
     dev = torch.device("cuda:0")
     wl = synth.workload(args.workload)
     if wl.pregrouped:
-        raise SystemExit("bench.py times token-major workloads; the pre-grouped layout is a parity case")
+        return bench_pregrouped(args, wl, dev)
     print(f"[bench] workload {wl.name}: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.k} {wl.wfmt}", file=sys.stderr,
           flush=True)
     x, ids_d, w_d, W, S, ids, w = make_inputs(wl, dev)
@@ -224,7 +324,7 @@ def main():
         del a, b
     torch.cuda.synchronize()
 
-    K = args.steps
+    K = args.steps if args.steps is not None else (200 if wl.wfmt == "mxfp4" else 20)
     evs = [hev.create(5) for _ in range(K)]
     revs = hev.create(K) if args.router else [None] * K
     torch.cuda.synchronize()

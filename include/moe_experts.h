@@ -249,6 +249,18 @@ typedef struct {
 int moe_route(const moe_route_problem* p, const float* logits, const float* bias, int32_t* topk_ids,
               float* topk_weights, moe_stream_t stream);
 
+/* moe_experts_forward_grouped that also records caller-created hipEvents on
+ * `stream` at its stage boundaries (stage_events[0] before the segment
+ * tables, [1] before GEMM1, [2] before GEMM2, [3] before the zero tail, [4]
+ * after it) so a benchmark can time each kernel on the stream it runs on.
+ * n_events must be 0 (no recording) or 5. */
+int moe_experts_forward_grouped_timed(const moe_problem* p, const void* x_nvs, const int32_t* cu_seqlens,
+                                      const float* route_w, const void* w_gate, const void* w_up,
+                                      const void* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                                      const uint8_t* s_down, void* out_nvs, void* workspace,
+                                      size_t workspace_bytes, moe_stream_t stream,
+                                      void* const* stage_events, int n_events);
+
 /* Reads the device status word of a workspace used by moe_experts_forward,
  * moe_experts_forward_grouped or moe_align: *n_bad = number of expert ids
  * outside [0, E) other than -1 in the last call (or 1 if its cu_seqlens were

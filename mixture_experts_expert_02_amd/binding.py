@@ -27,7 +27,7 @@ EXPORTED = (
     "moe_experts_workspace_bytes", "moe_experts_workspace_layout", "moe_experts_forward",
     "moe_experts_forward_timed", "moe_align_workspace_bytes", "moe_align",
     "moe_experts_grouped_workspace_bytes", "moe_experts_forward_grouped", "moe_device_error",
-    "moe_strerror", "moe_route",
+    "moe_strerror", "moe_route", "moe_experts_forward_grouped_timed",
 )
 MOE_ROUTE_RENORMALIZE, MOE_ROUTE_DEEPSEEK_V3 = 0, 1
 _ROUTE = {"renormalize": MOE_ROUTE_RENORMALIZE, "deepseek_v3": MOE_ROUTE_DEEPSEEK_V3}
@@ -86,6 +86,9 @@ def lib() -> ctypes.CDLL:
         L.moe_experts_grouped_workspace_bytes.restype = sz
         L.moe_experts_forward_grouped.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_experts_forward_grouped.restype = ctypes.c_int
+        L.moe_experts_forward_grouped_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                                        ctypes.POINTER(vp), ctypes.c_int]
+        L.moe_experts_forward_grouped_timed.restype = ctypes.c_int
         L.moe_device_error.argtypes = [vp, ctypes.POINTER(i32)]
         L.moe_device_error.restype = ctypes.c_int
         L.moe_route.argtypes = [ctypes.POINTER(MoeRouteProblem), vp, vp, vp, vp, vp]
@@ -169,6 +172,16 @@ def moe_experts_forward_grouped(p: MoeProblem, x_nvs, cu_seqlens, route_w, w_gat
                                              _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate), _ptr(s_up),
                                              _ptr(s_down), _ptr(out_nvs), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def moe_experts_forward_grouped_timed(p: MoeProblem, x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, s_gate,
+                                      s_up, s_down, out_nvs, workspace, events: Sequence[int], stream=None) -> int:
+    arr = (ctypes.c_void_p * len(events))(*events)
+    return lib().moe_experts_forward_grouped_timed(ctypes.byref(p), _ptr(x_nvs), _ptr(cu_seqlens), _ptr(route_w),
+                                                   _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate),
+                                                   _ptr(s_up), _ptr(s_down), _ptr(out_nvs), _ptr(workspace),
+                                                   workspace.numel() * workspace.element_size(), _stream(stream),
+                                                   arr, len(events))
 
 
 def moe_device_error(workspace) -> int:

@@ -531,20 +531,28 @@ size_t moe_experts_grouped_workspace_bytes(const moe_problem* p) {
   return make_plan(*p, true).total;
 }
 
-int moe_experts_forward_grouped(const moe_problem* p, const void* x_nvs, const int32_t* cu_seqlens,
-                                const float* route_w, const void* w_gate, const void* w_up, const void* w_down,
-                                const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down, void* out_nvs,
-                                void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int grouped_impl(const moe_problem* p, const void* x_nvs, const int32_t* cu_seqlens, const float* route_w,
+                 const void* w_gate, const void* w_up, const void* w_down, const uint8_t* s_gate,
+                 const uint8_t* s_up, const uint8_t* s_down, void* out_nvs, void* workspace,
+                 size_t workspace_bytes, hipStream_t s, void* const* ev, int n_ev) {
   int rc = check_problem(p, true);
   if (rc) return rc;
   if (!cu_seqlens || !route_w) return MOE_EINVAL;
   rc = check_common_ptrs(p, x_nvs, w_gate, w_up, w_down, s_gate, s_up, s_down, out_nvs, workspace);
   if (rc) return rc;
+  if (n_ev != 0 && (n_ev != 5 || !ev)) return MOE_EINVAL;
   if (p->T == 0) return MOE_OK;
   const Plan pl = make_plan(*p, true);
   if (workspace_bytes < pl.total) return MOE_ENOSPC;
-  hipStream_t s = (hipStream_t)stream;
+  auto mark = [&](int i) {
+    if (n_ev) hipEventRecord((hipEvent_t)ev[i], s);
+  };
   void* ws = workspace;
+  mark(0);
   moe::AlignOut o{};
   o.counts = at<int32_t>(ws, pl.counts);
   o.cu = at<int32_t>(ws, pl.cu);
@@ -564,20 +572,46 @@ int moe_experts_forward_grouped(const moe_problem* p, const void* x_nvs, const i
                        (const int32_t*)nullptr, 1, route_w, (const int32_t*)nullptr, p->T, p->H,
                        at<uint16_t>(ws, pl.xs));
   }
+  mark(1);
   if (mx) {
     g1.Aq = quant_rows_at(ws, pl.xq, pl.M, p->H);
     launch_quant(g1.A, pl.M, p->H, g1.Aq, s);
   }
   if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
   GemmIO g2{at<void>(ws, pl.act), nullptr, 1, w_down, nullptr, s_down, nullptr, p->H, p->I, out_nvs, nullptr, 1, 0, {}};
+  mark(2);
   if (mx) {
     g2.Aq = quant_rows_at(ws, pl.aq, pl.M, p->I);
     launch_quant(g2.A, pl.M, p->I, g2.Aq, s);
   }
   if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
+  mark(3);
   hipLaunchKernelGGL(moe::k_zero_tail, dim3(p->T), dim3(256), 0, s, (uint16_t*)out_nvs,
                      (const int32_t*)o.status, p->T, p->H);
+  mark(4);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_experts_forward_grouped(const moe_problem* p, const void* x_nvs, const int32_t* cu_seqlens,
+                                const float* route_w, const void* w_gate, const void* w_up, const void* w_down,
+                                const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down, void* out_nvs,
+                                void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  return grouped_impl(p, x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, s_gate, s_up, s_down, out_nvs,
+                      workspace, workspace_bytes, (hipStream_t)stream, nullptr, 0);
+}
+
+int moe_experts_forward_grouped_timed(const moe_problem* p, const void* x_nvs, const int32_t* cu_seqlens,
+                                      const float* route_w, const void* w_gate, const void* w_up,
+                                      const void* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                                      const uint8_t* s_down, void* out_nvs, void* workspace,
+                                      size_t workspace_bytes, moe_stream_t stream, void* const* stage_events,
+                                      int n_events) {
+  return grouped_impl(p, x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, s_gate, s_up, s_down, out_nvs,
+                      workspace, workspace_bytes, (hipStream_t)stream, stage_events, n_events);
 }
 
 int moe_route(const moe_route_problem* p, const float* logits, const float* bias, int32_t* topk_ids,

@@ -206,3 +206,12 @@ def test_weight_on_input_workspace_holds_scaled_rows():
     g0 = B.problem(100, 128, 256, 5)
     g1 = B.problem(100, 128, 256, 5, weight_on_input=True)
     assert B.moe_experts_grouped_workspace_bytes(g1) >= B.moe_experts_grouped_workspace_bytes(g0) + 100 * 128 * 2
+
+
+def test_grouped_timed_event_count_checked():
+    L = B.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    g = B.problem(100, 128, 256, 5)
+    ev = (ctypes.c_void_p * 3)()
+    assert L.moe_experts_forward_grouped_timed(ctypes.byref(g), fake, fake, fake, fake, fake, fake, None, None, None,
+                                               fake, fake, 1 << 40, None, ev, 3) == B.MOE_EINVAL

@@ -254,3 +254,27 @@ def test_grouped_malformed_offsets_flagged_and_zero():
     torch.cuda.synchronize()
     assert B.moe_device_error(ws) == 1
     assert torch.all(out == 0)
+
+
+def test_grouped_timed_matches_untimed_bitwise():
+    """moe_experts_forward_grouped_timed only adds event records."""
+    import ctypes
+    x, cu, rw, W, S = grouped_case(11, [300, 0, 257, 1], 9)
+    G, H, I = 4, 256, 384
+    p = B.problem(x.shape[0], H, I, G, 1)
+    ws = B.alloc_workspace(B.moe_experts_grouped_workspace_bytes(p), DEV)
+    args = [x.to(DEV), torch.from_numpy(cu).to(DEV), torch.from_numpy(rw).to(DEV), *[t.to(DEV) for t in W]]
+    ref = B.experts_forward_grouped(*args, workspace=ws)
+    hip = ctypes.CDLL("libamdhip64.so")
+    evs = []
+    for _ in range(5):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    out = torch.empty_like(ref)
+    rc = B.moe_experts_forward_grouped_timed(p, *args, None, None, None, out, ws, evs)
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert torch.equal(out, ref)
+    for e in evs:
+        hip.hipEventDestroy(ctypes.c_void_p(e))

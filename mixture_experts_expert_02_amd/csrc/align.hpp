@@ -144,8 +144,8 @@ __device__ void finish_tables(const int32_t* cnt, const int32_t* off, int32_t* m
 // One-workgroup path (small M, E <= 1024): count, scan and scatter in one launch.
 // LDS: hist[4][E] + cnt[E] + off[E] + mt[E] + 16 ints.
 // ------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_align_fused(const int32_t* ids, const float* w, int M, int E,
-                                                     int nbits, int BM, AlignOut o) {
+__device__ __forceinline__ void align_fused_body(const int32_t* ids, const float* w, int M, int E, int nbits,
+                                                 int BM, const AlignOut& o) {
   extern __shared__ int32_t lds[];
   int32_t* hist = lds;            // [4][E]
   int32_t* cnt = hist + 4 * E;    // [E]
@@ -178,6 +178,11 @@ __global__ __launch_bounds__(256) void k_align_fused(const int32_t* ids, const f
   __syncthreads();
   wave_scatter(ids, w, begin, end, E, nbits, hist + wid * E, o);
   finish_tables<256>(cnt, off, mts, E, M, total, BM, total_bad, o, scratch);
+}
+
+__global__ __launch_bounds__(256) void k_align_fused(const int32_t* ids, const float* w, int M, int E,
+                                                     int nbits, int BM, AlignOut o) {
+  align_fused_body(ids, w, M, E, nbits, BM, o);
 }
 
 // ------------------------------------------------------------------------

@@ -105,14 +105,9 @@ struct Params {
   ActParams act;
 };
 
-// One workgroup per row, one 32-value block per thread. With perm, output
-// row r is source row perm[r] / div (sorted row -> token), for the first
-// status[1] rows (the valid sorted rows; the rest are never read).
-__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ src, int rows, int K, QRows q,
-                                                    const int32_t* perm, int div, const int32_t* status) {
-  const int r = blockIdx.x;
-  if (r >= rows || (perm && r >= status[1])) return;
-  const size_t sr = perm ? (size_t)(perm[r] / div) : (size_t)r;
+// Split row r of q from bf16 source row sr (256 threads, one 32-value block
+// per thread and step).
+__device__ __forceinline__ void quant_row(const uint16_t* __restrict__ src, size_t sr, int r, int K, const QRows& q) {
   const int KB = K / 32;
   for (int b = threadIdx.x; b < q.sc_stride; b += 256) {
     if (b >= KB) {
@@ -152,6 +147,16 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
     lw[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
     q.sc[(size_t)r * q.sc_stride + b] = (uint8_t)code;
   }
+}
+
+// One workgroup per row. With perm, output row r is source row perm[r] / div
+// (sorted row -> token), for the first status[1] rows (the valid sorted rows;
+// the rest are never read).
+__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ src, int rows, int K, QRows q,
+                                                    const int32_t* perm, int div, const int32_t* status) {
+  const int r = blockIdx.x;
+  if (r >= rows || (perm && r >= status[1])) return;
+  quant_row(src, perm ? (size_t)(perm[r] / div) : (size_t)r, r, K, q);
 }
 
 template <int FMT>

@@ -18,6 +18,7 @@
 #include "combine.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_skinny.hpp"
+#include "decode_prologue.hpp"
 #include "router.hpp"
 #include "scale_rows.hpp"
 
@@ -401,17 +402,30 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
   o.status = at<int32_t>(ws, pl.status);
   const int M = (int)pl.M;
 
-  mark(0);
-  if ((rc = launch_align(ids, tw, M, p->E, pl.BM, pl, o, ws, s))) return rc;
-
   const bool mx = p->wfmt == MOE_W_MXFP4;
+  // MXFP4 with the one-workgroup align: x split in token order in the same
+  // launch (GEMM1 reads it through the permutation)
+  const bool mx_prologue = mx && pl.fused_align && !p->weight_on_input;
+  mark(0);
+  if (mx_prologue) {
+    const size_t lds = (size_t)(7 * p->E + 16) * 4;
+    hipLaunchKernelGGL(moe::k_align_fused_quant, dim3((unsigned)p->T + 1), dim3(256), lds, s, ids, tw, M, p->E,
+                       bits_for(p->E), pl.BM, o, (const uint16_t*)x, p->T, p->H,
+                       quant_rows_at(ws, pl.xq, p->T, p->H));
+    if ((rc = launch_status())) return rc;
+  } else if ((rc = launch_align(ids, tw, M, p->E, pl.BM, pl, o, ws, s))) {
+    return rc;
+  }
+
   GemmIO g1{x, o.perm, p->k, wg, wu, sg, su, p->I, p->H, at<void>(ws, pl.act), o.w_sorted, 1, 0, {}};
   if (p->weight_on_input) {  // rows x * w in sorted order; no weight in GEMM1's epilogue
     g1.A = at<void>(ws, pl.xs);
     g1.a_perm = nullptr;
     g1.row_w = nullptr;
   }
-  if (mx) {  // x split in sorted row order: GEMM1 reads its rows without the permutation
+  if (mx_prologue) {  // x split in token order by the prologue
+    g1.Aq = quant_rows_at(ws, pl.xq, p->T, p->H);
+  } else if (mx) {  // x split in sorted row order: GEMM1 reads its rows without the permutation
     g1.Aq = quant_rows_at(ws, pl.xq, pl.M, p->H);
     g1.a_perm = nullptr;
   }
@@ -420,7 +434,7 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
     hipLaunchKernelGGL(moe::k_scale_rows, dim3((unsigned)pl.M), dim3(256), 0, s, (const uint16_t*)x,
                        (const int32_t*)o.perm, p->k, (const float*)o.w_sorted, (const int32_t*)o.status, M, p->H,
                        at<uint16_t>(ws, pl.xs));
-  if (mx) {
+  if (mx && !mx_prologue) {
     if (p->weight_on_input) launch_quant(g1.A, pl.M, p->H, g1.Aq, s);
     else launch_quant(x, pl.M, p->H, g1.Aq, s, o.perm, p->k, o.status);
   }

@@ -87,6 +87,8 @@ CASES = [
     ("decode_mxfp4_k8192", (4, 8192, 256, 3, 2), "mxfp4", "swiglu_oai", {}),
     ("decode_mxfp4_k16384", (3, 256, 16384, 2, 1), "mxfp4", "silu", {}),
     ("decode_mxfp4_k6144_ragged", (5, 6144, 320, 3, 2), "mxfp4", "silu", {}),
+    # more than 4096 routed rows: the chunked align and the sorted-order x split
+    ("mxfp4_chunked_align", (2100, 128, 256, 4, 2), "mxfp4", "swiglu_oai", {"masked": 0.05}),
 ]
 ACT_PARAMS = {"silu": {}, "swiglu_oai": dict(alpha=1.702, beta=1.0, limit=7.0), "situ": dict(alpha=1.5, beta=0.8)}
 

@@ -89,6 +89,8 @@ CASES = [
     ("decode_mxfp4_k6144_ragged", (5, 6144, 320, 3, 2), "mxfp4", "silu", {}),
     # more than 4096 routed rows: the chunked align and the sorted-order x split
     ("mxfp4_chunked_align", (2100, 128, 256, 4, 2), "mxfp4", "swiglu_oai", {"masked": 0.05}),
+    # MXFP4 decode with masked and bad ids: tokens whose slots are all dead get zero rows
+    ("decode_mxfp4_masked_bad", (40, 256, 320, 6, 3), "mxfp4", "swiglu_oai", {"masked": 0.3, "bad": 0.1}),
 ]
 ACT_PARAMS = {"silu": {}, "swiglu_oai": dict(alpha=1.702, beta=1.0, limit=7.0), "situ": dict(alpha=1.5, beta=0.8)}
 

@@ -11,9 +11,12 @@ I=14336, E=8, top-2, bf16), reported in TFLOP/s of routed-row GEMM work.
 --workload pregrouped times the pre-grouped entry (segments already
 contiguous, caller's cu_seqlens) instead of the token-major step.
 
-Per-kernel times come from hipEvents that the library records between its
-launches on the benchmark's stream (moe_experts_forward_timed), over the same
-timed steps.
+The K timed steps run twice after the warm-up: first with hipEvents that the
+library records between its launches on the benchmark's stream
+(moe_experts_forward_timed), which give the per-kernel times (stage_ms, the
+roofline's kernel time) and the instrumented pass's own wall-clock time,
+then with no instrumentation: that pass's wall-clock time gives ms_per_step
+and value.
 """
 from __future__ import annotations
 
@@ -49,6 +52,29 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
+
+
+def timed_passes(step, K, hev, n_ev, extra=None):
+    """K steps with n_ev events per step (and one more per step when extra is
+    set), then K steps with no events, whose wall-clock time is the step time
+    (an event record between two launches leaves a gap on the stream: about
+    14 us per decode step of 0.22 ms). Returns (ms_per_step, instrumented
+    ms_per_step, events, extra events)."""
+    import torch
+    evs = [hev.create(n_ev) for _ in range(K)]
+    xevs = hev.create(K) if extra else [None] * K
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs[i], xevs[i])
+    torch.cuda.synchronize()
+    instr = (time.perf_counter() - t0) * 1e3 / K
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    plain = (time.perf_counter() - t0) * 1e3 / K
+    return plain, instr, evs, xevs
 
 
 class HipEvents:
@@ -218,7 +244,7 @@ def bench_pregrouped(args, wl, dev):
     stream = torch.cuda.current_stream()
     hev = HipEvents()
 
-    def step(evs=()):
+    def step(evs=(), _unused=None):
         rc = B.moe_experts_forward_grouped_timed(p, x, cu_d, rw_d, *W, None, None, None, out, ws, list(evs),
                                                  stream=stream)
         if rc != 0:
@@ -233,19 +259,12 @@ def bench_pregrouped(args, wl, dev):
         del a, b
     torch.cuda.synchronize()
     K = args.steps if args.steps is not None else 20
-    evs = [hev.create(5) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    ms_per_step, instr_ms, evs, _ = timed_passes(step, K, hev, 5)
     stages = ("prep", "gemm1", "gemm2", "zero_tail")
     avg = {s: float(np.mean([hev.elapsed_ms(e[j], e[j + 1]) for e in evs])) for j, s in enumerate(stages)}
     step_ms = float(np.mean([hev.elapsed_ms(e[0], e[4]) for e in evs]))
     for e in evs:
         hev.destroy(e)
-    ms_per_step = wall * 1e3 / K
     M = int(cu[-1])
     n_touched = int(np.sum(lengths > 0))
     value = 6.0 * M * wl.H * wl.I / (ms_per_step * 1e-3) / 1e12
@@ -262,6 +281,7 @@ def bench_pregrouped(args, wl, dev):
                    "activation": wl.act, "routed_rows": M, "touched_experts": n_touched},
         "stage_ms": {s: round(v, 4) for s, v in avg.items()},
         "event_ms_per_step": round(step_ms, 4),
+        "instrumented_ms_per_step": round(instr_ms, 4),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
@@ -325,14 +345,7 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps if args.steps is not None else (200 if wl.wfmt == "mxfp4" else 20)
-    evs = [hev.create(5) for _ in range(K)]
-    revs = hev.create(K) if args.router else [None] * K
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(evs[i], revs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    ms_per_step, instr_ms, evs, revs = timed_passes(step, K, hev, 5, extra=args.router)
     stage_ms = {s: [] for s in (("router",) if args.router else ()) + STAGES}
     for e, r in zip(evs, revs):
         for j, s in enumerate(STAGES):
@@ -344,7 +357,6 @@ def main():
         hev.destroy(e)
     if args.router:
         hev.destroy(revs)
-    ms_per_step = wall * 1e3 / K
 
     M = wl.T * wl.k
     n_touched, wbytes = touched_weight_bytes(wl, ids)
@@ -377,6 +389,7 @@ def main():
                    "weights": wl.wfmt, "activation": wl.act, "routed_rows": M, "touched_experts": n_touched},
         "stage_ms": {s: round(v, 4) for s, v in avg.items()},
         "event_ms_per_step": round(float(np.mean(step_ms)), 4),
+        "instrumented_ms_per_step": round(instr_ms, 4),
         "roofline": roof,
     }
     if args.router:

@@ -31,6 +31,16 @@ Readings where the pages are silent:
     id outside [0, E) is skipped and counted as bad.
   * Combine sums the k slot results of a token in ascending j.
 
+  * MXFP8 activations (act_fmt="mxfp8"): the trtllm_mxfp4_moe page lists
+    MXFP4 weights with dynamically quantized MXFP8 activations as a supported
+    scheme but gives no formula. Reading: OCP Microscaling v1.0 with e4m3
+    elements: per 32 consecutive values of a row along K, the scale is
+    X = 2^(floor(log2(amax)) - 8) (8 = the e4m3 largest exponent), its e8m0
+    code clamped to [0, 254] (code 0 when amax = 0); each value becomes
+    rne_e4m3(v / X), saturated at +-448, times X. Both GEMM inputs are
+    quantized this way: the token rows before the gate and up GEMMs, the
+    activation rows (after the route weight) before the down GEMM.
+
 Everything is computed in float64 from exactly widened inputs.
 """
 from __future__ import annotations
@@ -42,7 +52,7 @@ import numpy as np
 
 __all__ = [
     "align", "grouped_mm", "silu", "swiglu_oai", "situ", "activation",
-    "mxfp4_decode", "expert_matrix", "experts_grouped", "experts_forward",
+    "mxfp4_decode", "e4m3_round", "mxfp8_quantize", "expert_matrix", "experts_grouped", "experts_forward",
     "experts_forward_literal", "pregrouped_forward",
 ]
 
@@ -175,6 +185,59 @@ def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return val * sc
 
 
+# ----------------------------------------------------------------------------
+# MXFP8 activations (OCP Microscaling v1.0 reading with e4m3 elements; the
+# trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsBase, names the scheme only).
+# ----------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_round(v) -> np.ndarray:
+    """Nearest e4m3 value, ties to even, magnitudes above 448 saturated to 448.
+
+    e4m3 (the OCP "fn" variant): sign, 4 exponent bits with bias 7, 3 mantissa
+    bits; normal values 2^(e-7) (1 + m/8) for e = 1..15 (e = 15, m = 7 is NaN,
+    so 448 is the largest), subnormal values 2^-6 m/8. Inside the binade
+    [2^b, 2^(b+1)) the spacing is 2^(b-3); below 2^-6 it is 2^-9."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(a)                      # a = f 2^ex, f in [0.5, 1): floor(log2 a) = ex - 1
+    b = np.maximum(ex - 1, -6)
+    q = np.ldexp(1.0, (b - 3).astype(np.int32))
+    r = np.round(a / q) * q                  # a / q is exact; np.round ties to even
+    return np.sign(v) * np.minimum(r, E4M3_MAX)
+
+
+def mxfp8_quantize(a: np.ndarray):
+    """MXFP8 (e4m3 elements) quantization of the last axis in blocks of 32.
+
+    Returns (values, elements, codes): values = elements * 2^(codes - 127) in
+    float64; elements are the e4m3 values; codes the e8m0 scale bytes, one per
+    block: floor(log2(amax)) + 127 - 8 clamped to [0, 254], and 0 for an
+    all-zero block."""
+    a = np.asarray(a, dtype=np.float64)
+    K = a.shape[-1]
+    if K % 32:
+        raise ValueError("MXFP8 needs the last axis to be a multiple of 32")
+    blk = a.reshape(*a.shape[:-1], K // 32, 32)
+    amax = np.max(np.abs(blk), axis=-1)
+    _, ex = np.frexp(amax)
+    code = np.where(amax > 0, np.clip(ex - 1 + 127 - 8, 0, 254), 0).astype(np.int64)
+    X = np.ldexp(1.0, (code - 127).astype(np.int32))[..., None]
+    elem = e4m3_round(blk / X)
+    vals = (elem * X).reshape(a.shape)
+    return vals, elem.reshape(a.shape), code.astype(np.uint8)
+
+
+def _act_in(rows: np.ndarray, act_fmt: str) -> np.ndarray:
+    """A GEMM's input rows as the GEMM sees them."""
+    if act_fmt == "bf16":
+        return rows
+    if act_fmt == "mxfp8":
+        return mxfp8_quantize(rows)[0]
+    raise ValueError(f"unknown activation format {act_fmt!r}")
+
+
 def expert_matrix(w: Weight, e: int) -> np.ndarray:
     """Expert e's [N, K] weight in float64 (decoded when MXFP4)."""
     if isinstance(w, tuple):
@@ -190,7 +253,7 @@ def expert_matrix(w: Weight, e: int) -> np.ndarray:
 def experts_grouped(x_rows: np.ndarray, cu_seqlens: Sequence[int], route_w: np.ndarray,
                     w_gate: Weight, w_up: Weight, w_down: Weight,
                     act: str = "silu", alpha=1.0, beta=0.0, limit=math.inf,
-                    weight_on_input: bool = False) -> np.ndarray:
+                    weight_on_input: bool = False, act_fmt: str = "bf16") -> np.ndarray:
     """Rows already contiguous per weight row: gate and up grouped GEMMs, the
     activation times the per-row route weight, the down grouped GEMM. Rows past
     the last end offset come out zero.
@@ -198,13 +261,17 @@ def experts_grouped(x_rows: np.ndarray, cu_seqlens: Sequence[int], route_w: np.n
     weight_on_input: the route weight multiplies the input row before the gate
     and up GEMMs instead of the activation (moonep_experts page,
     MoonEPExperts.apply: input-weighted routing is applied to the activations
-    before dispatch, and the experts step then skips its own multiply)."""
+    before dispatch, and the experts step then skips its own multiply).
+
+    act_fmt "mxfp8": both GEMMs' input rows are MXFP8-quantized first (the
+    reading in the module docstring)."""
     x_rows = np.asarray(x_rows, dtype=np.float64)
     NvS = x_rows.shape[0]
     H = x_rows.shape[1]
     rw = np.asarray(route_w, dtype=np.float64)[:, None]
     if weight_on_input:
         x_rows = x_rows * rw
+    x_rows = _act_in(x_rows, act_fmt)
     gate = grouped_mm(x_rows, lambda g: expert_matrix(w_gate, g), cu_seqlens)
     if gate is None:                                    # every segment empty
         return np.zeros((NvS, H), dtype=np.float64)
@@ -212,6 +279,7 @@ def experts_grouped(x_rows: np.ndarray, cu_seqlens: Sequence[int], route_w: np.n
     a = activation(act, gate, up, alpha, beta, limit)
     if not weight_on_input:
         a = a * rw
+    a = _act_in(a, act_fmt)
     out = grouped_mm(a, lambda g: expert_matrix(w_down, g), cu_seqlens)
     end = int(cu_seqlens[-1]) if len(cu_seqlens) else 0
     out[end:] = 0.0
@@ -221,7 +289,7 @@ def experts_grouped(x_rows: np.ndarray, cu_seqlens: Sequence[int], route_w: np.n
 def experts_forward(x: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
                     w_gate: Weight, w_up: Weight, w_down: Weight,
                     act: str = "silu", alpha=1.0, beta=0.0, limit=math.inf,
-                    weight_on_input: bool = False) -> np.ndarray:
+                    weight_on_input: bool = False, act_fmt: str = "bf16") -> np.ndarray:
     """Token-major MoE experts layer: group the routed slots by expert, run
     the grouped computation, then combine each token's k slot results in
     ascending j (flashinfer_moe_ep page: route, compute, combine)."""
@@ -234,7 +302,7 @@ def experts_forward(x: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarra
     x_rows = x[perm // k]
     rw = np.asarray(topk_weights, dtype=np.float64).reshape(-1)[perm]
     y = experts_grouped(x_rows, al["cu_seqlens"], rw, w_gate, w_up, w_down, act, alpha, beta, limit,
-                        weight_on_input)
+                        weight_on_input, act_fmt)
     out = np.zeros((T, x.shape[1]), dtype=np.float64)
     for t in range(T):
         acc = np.zeros(x.shape[1], dtype=np.float64)
@@ -248,7 +316,7 @@ def experts_forward(x: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarra
 
 def experts_forward_literal(x, topk_ids, topk_weights, w_gate, w_up, w_down,
                             act="silu", alpha=1.0, beta=0.0, limit=math.inf,
-                            weight_on_input=False) -> np.ndarray:
+                            weight_on_input=False, act_fmt="bf16") -> np.ndarray:
     """The per-token definition: for each token and each of its k slots, run
     the selected expert's MLP on the token, scale by the route weight, and sum
     over the slots in ascending j. Masked (-1) and out-of-range ids add
@@ -266,23 +334,26 @@ def experts_forward_literal(x, topk_ids, topk_weights, w_gate, w_up, w_down,
             if e < 0 or e >= E:
                 continue
             xin = x[t] * wts[t, j] if weight_on_input else x[t]
+            xin = _act_in(xin, act_fmt)
             g = expert_matrix(w_gate, e) @ xin
             u = expert_matrix(w_up, e) @ xin
             a = activation(act, g, u, alpha, beta, limit)
             if not weight_on_input:
                 a = a * wts[t, j]
+            a = _act_in(a, act_fmt)
             acc = acc + expert_matrix(w_down, e) @ a
         out[t] = acc
     return out
 
 
 def pregrouped_forward(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down,
-                       act="silu", alpha=1.0, beta=0.0, limit=math.inf, weight_on_input=False) -> np.ndarray:
+                       act="silu", alpha=1.0, beta=0.0, limit=math.inf, weight_on_input=False,
+                       act_fmt="bf16") -> np.ndarray:
     """The pre-grouped entry: rows given in segment order with end offsets and
     per-row route weights (moonep_experts page, MoonEPExperts.apply). Same as
     `experts_grouped`; named for the entry point it checks."""
     return experts_grouped(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, act, alpha, beta, limit,
-                           weight_on_input)
+                           weight_on_input, act_fmt)
 
 
 def _num_experts(w: Weight) -> int:

@@ -463,3 +463,116 @@ def test_situ_forward_top1_is_dense_situ_mlp():
     g, u = X @ G.T, X @ U.T
     want = ((al * torch.tanh(g / al) * torch.sigmoid(g)) * (be * torch.tanh(u / be))) @ D.T
     np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ MXFP8 activations
+def _e4m3_table():
+    """All finite e4m3 (fn) values from their bit patterns: sign, 4 exponent
+    bits (bias 7), 3 mantissa bits; exponent 15 with mantissa 7 is NaN."""
+    vals = {}
+    for code in range(256):
+        s, e, m = code >> 7, (code >> 3) & 15, code & 7
+        if e == 15 and m == 7:
+            continue
+        mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+        vals[code] = -mag if s else mag
+    return vals
+
+
+def test_e4m3_round_exhaustive_grid_midpoints_and_saturation():
+    table = _e4m3_table()
+    grid = np.array(sorted({v for v in table.values() if v >= 0}))
+    assert grid[-1] == 448.0 and len(grid) == 127
+    assert np.array_equal(oracle.e4m3_round(grid), grid)
+    assert np.array_equal(oracle.e4m3_round(-grid), -grid)
+    # a midpoint goes to the neighbour whose mantissa bit 0 is clear
+    even = {v: (c & 1) == 0 for c, v in table.items() if v >= 0}
+    lo, hi = grid[:-1], grid[1:]
+    mid = (lo + hi) / 2
+    want = np.where([even[a] for a in lo], lo, hi)
+    assert np.array_equal(oracle.e4m3_round(mid), want)
+    # just off the midpoint goes to the nearer neighbour
+    assert np.array_equal(oracle.e4m3_round(mid - (hi - lo) * 1e-3), lo)
+    assert np.array_equal(oracle.e4m3_round(mid + (hi - lo) * 1e-3), hi)
+    big = np.array([448.5, 463.9, 464.0, 480.0, 1e6])
+    assert np.array_equal(oracle.e4m3_round(big), np.full(5, 448.0))
+    assert np.array_equal(oracle.e4m3_round(-big), np.full(5, -448.0))
+
+
+def test_e4m3_round_matches_torch_float8_in_range():
+    # torch's float8_e4m3fn conversion (round to nearest even) on float32
+    # inputs inside the finite range
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.uniform(-4, 2.5, 20000),
+                        rng.uniform(-448, 448, 5000)]).astype(np.float32)
+    v = v[np.abs(v) <= 448]          # torch gives NaN past the range; the oracle saturates
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(oracle.e4m3_round(v.astype(np.float64)), ref)
+
+
+def test_mxfp8_quantize_closed_forms():
+    # amax 1 -> X = 2^-8 (code 119): 0.1 * 256 = 25.6 lies in [16, 32), spacing 2 -> 26
+    v, e, c = oracle.mxfp8_quantize(np.array([[1.0, 0.1, 0.01] + [0.0] * 29]))
+    assert c.tolist() == [[119]]
+    assert v[0, :3].tolist() == [1.0, 26 / 256, 2.5 / 256]
+    assert e[0, :3].tolist() == [256.0, 26.0, 2.5]
+    # amax 1.9: 1.9 * 256 = 486.4 saturates at 448 -> 1.75
+    v, e, c = oracle.mxfp8_quantize(np.array([[-1.9] + [0.25] * 31]))
+    assert c.tolist() == [[119]] and v[0, 0] == -1.75 and e[0, 0] == -448.0 and v[0, 1] == 0.25
+    # an all-zero block: code 0, zeros; scale codes clamp at both ends
+    v, e, c = oracle.mxfp8_quantize(np.zeros((1, 64)))
+    assert c.tolist() == [[0, 0]] and not v.any()
+    _, _, c = oracle.mxfp8_quantize(np.array([[2.0 ** -130] + [0.0] * 31, [2.0 ** 200] + [0.0] * 31]))
+    assert c.ravel().tolist() == [0, 254]
+    with pytest.raises(ValueError):
+        oracle.mxfp8_quantize(np.zeros((2, 48)))
+
+
+def test_mxfp8_values_on_the_grid_are_fixed_points():
+    # blocks built as e4m3 values times 2^(c-127), with one element in
+    # [256, 448] so that the block's own scale is 2^(c-127): unchanged
+    rng = np.random.default_rng(4)
+    grid = np.array(sorted(set(_e4m3_table().values())))
+    top = grid[(np.abs(grid) >= 256)]
+    rows = []
+    codes = rng.integers(1, 240, size=40)
+    for c in codes:
+        el = rng.choice(grid, size=32)
+        el = np.where(np.abs(el) > 448, 448.0, el)
+        el[rng.integers(32)] = rng.choice(top)
+        rows.append(el * 2.0 ** (int(c) - 127))
+    a = np.array(rows)
+    v, e, cq = oracle.mxfp8_quantize(a)
+    assert np.array_equal(v, a)
+    assert cq.ravel().tolist() == codes.tolist()
+
+
+def test_mxfp8_error_bound_on_random_rows():
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((64, 256)) * 10.0 ** rng.uniform(-3, 3, (64, 1))
+    v, e, c = oracle.mxfp8_quantize(a)
+    X = np.repeat(np.ldexp(1.0, c.astype(np.int32) - 127), 32, axis=-1)
+    r = np.abs(a) / X
+    err = np.abs(v - a) / X
+    _, ex = np.frexp(r)
+    half_ulp = np.ldexp(1.0, np.maximum(ex - 1, -6) - 4)    # half the spacing 2^(b-3)
+    sat = r > 448
+    assert np.all(err[~sat] <= half_ulp[~sat])
+    # saturation happens only in blocks whose amax / X reaches 464 (mantissa >= 1.8125)
+    assert np.all(r[sat] >= 448)
+    assert np.all(np.abs(e) <= 448)
+
+
+def test_mxfp8_forward_grouped_equals_literal_and_differs_from_exact():
+    x, ids, w, wg, wu, wd = rand_problem(21, T=7, H=64, I=96, E=4, k=2, masked=0.2)
+    for woi in (False, True):
+        a = oracle.experts_forward(x, ids, w, wg, wu, wd, weight_on_input=woi, act_fmt="mxfp8")
+        b = oracle.experts_forward_literal(x, ids, w, wg, wu, wd, weight_on_input=woi, act_fmt="mxfp8")
+        assert np.max(np.abs(a - b)) <= 1e-12 * np.max(np.abs(b))
+        exact = oracle.experts_forward(x, ids, w, wg, wu, wd, weight_on_input=woi)
+        d = np.max(np.abs(a - exact)) / np.max(np.abs(exact))
+        assert 1e-4 < d < 0.1        # e4m3 keeps 4 significant bits
+    # on-grid inputs are not changed by the first quantization: with the
+    # activation left exact, gate and up see x itself
+    with pytest.raises(ValueError):
+        oracle.experts_forward(x, ids, w, wg, wu, wd, act_fmt="fp4")

@@ -39,7 +39,10 @@ Readings where the pages are silent:
     code clamped to [0, 254] (code 0 when amax = 0); each value becomes
     rne_e4m3(v / X), saturated at +-448, times X. Both GEMM inputs are
     quantized this way: the token rows before the gate and up GEMMs, the
-    activation rows (after the route weight) before the down GEMM.
+    activation rows (after the route weight) before the down GEMM. The
+    quantizer's input is a bf16 activation tensor (the model's activations
+    are bf16; the scheme quantizes them dynamically), so a row computed here
+    in float64 is rounded to bf16 (to nearest even) first.
 
 Everything is computed in float64 from exactly widened inputs.
 """
@@ -52,7 +55,7 @@ import numpy as np
 
 __all__ = [
     "align", "grouped_mm", "silu", "swiglu_oai", "situ", "activation",
-    "mxfp4_decode", "e4m3_round", "mxfp8_quantize", "expert_matrix", "experts_grouped", "experts_forward",
+    "mxfp4_decode", "e4m3_round", "mxfp8_quantize", "bf16_round", "expert_matrix", "experts_grouped", "experts_forward",
     "experts_forward_literal", "pregrouped_forward",
 ]
 
@@ -229,12 +232,22 @@ def mxfp8_quantize(a: np.ndarray):
     return vals, elem.reshape(a.shape), code.astype(np.uint8)
 
 
+def bf16_round(v) -> np.ndarray:
+    """Nearest bf16 value (8 significant bits), ties to even, for finite
+    values in the normal range: inside [2^b, 2^(b+1)) the spacing is 2^(b-7)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(a)
+    q = np.ldexp(1.0, (ex - 1 - 7).astype(np.int32))
+    return np.sign(v) * np.round(a / q) * q
+
+
 def _act_in(rows: np.ndarray, act_fmt: str) -> np.ndarray:
     """A GEMM's input rows as the GEMM sees them."""
     if act_fmt == "bf16":
         return rows
     if act_fmt == "mxfp8":
-        return mxfp8_quantize(rows)[0]
+        return mxfp8_quantize(bf16_round(rows))[0]
     raise ValueError(f"unknown activation format {act_fmt!r}")
 
 

@@ -576,3 +576,33 @@ def test_mxfp8_forward_grouped_equals_literal_and_differs_from_exact():
     # activation left exact, gate and up see x itself
     with pytest.raises(ValueError):
         oracle.experts_forward(x, ids, w, wg, wu, wd, act_fmt="fp4")
+
+
+def test_bf16_round_matches_torch_and_closed_forms():
+    # torch's float32 -> bfloat16 conversion (round to nearest even) on float32 inputs
+    rng = np.random.default_rng(8)
+    v = (rng.standard_normal(50000) * 10.0 ** rng.uniform(-20, 20, 50000)).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.bf16_round(v.astype(np.float64)), ref)
+    # 1 + 2^-8 is the midpoint of 1 and 1 + 2^-7: ties to even (1); just above goes up
+    assert oracle.bf16_round(np.array([1 + 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20, 3 * 2.0 ** -9 + 1])).tolist() == \
+        [1.0, 1 + 2.0 ** -7, 1 + 2.0 ** -7]
+    assert oracle.bf16_round(np.array([0.0, -2.0 ** 100])).tolist() == [0.0, -2.0 ** 100]
+
+
+def test_mxfp8_mode_quantizes_the_bf16_activation():
+    # bf16 values are unchanged by the bf16 rounding, so on bf16 input rows the
+    # mode's first quantization is exactly mxfp8_quantize
+    rng = np.random.default_rng(9)
+    rows = torch.from_numpy(rng.standard_normal((4, 64)).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(oracle.moe_oracle._act_in(rows, "mxfp8"), oracle.mxfp8_quantize(rows)[0])
+    # an off-grid value that bf16 rounding moves onto an e4m3 midpoint: in a
+    # block of amax 1.5 (scale 2^-8) the e4m3 neighbours of 1 + 2^-4 are 1 and
+    # 1 + 2^-3; 1 + 2^-4 + 2^-10 rounds to 1 + 2^-4 in bf16 (8 bits), then to 1
+    # (even) in e4m3, while unrounded it goes up to 1 + 2^-3
+    blk = np.zeros((1, 32))
+    blk[0, 0] = 1.5
+    blk[0, 1] = 1 + 2.0 ** -4 + 2.0 ** -10
+    got = oracle.moe_oracle._act_in(blk, "mxfp8")
+    assert got[0, 1] == 1.0
+    assert oracle.mxfp8_quantize(blk)[0][0, 1] == 1 + 2.0 ** -3

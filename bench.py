@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--print-source-hash", action="store_true")
     ap.add_argument("--router", action="store_true",
                     help="run the router (moe_route, Renormalize) on the workload's logits inside each step")
+    ap.add_argument("--act-fmt", default="bf16", choices=("bf16", "mxfp8"),
+                    help="activation format of the GEMM inputs (mxfp8: MXFP4-weight workloads only)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -181,14 +183,14 @@ def subproblem_host(wl, x, ids, w, W, S, n_tokens):
     return xs, ids_c, w[:n_tokens], Wh
 
 
-def cpu_baseline(wl, x, ids, w, W, S, n_tokens):
+def cpu_baseline(wl, x, ids, w, W, S, n_tokens, act_fmt="bf16"):
     """The CPU oracle, as it is, on the first n_tokens tokens of the workload."""
     import numpy as np
     import threadpoolctl
     import oracle
     n_tokens = min(n_tokens, wl.T)
     xs, ids_c, ws_, Wh = subproblem_host(wl, x, ids, w, W, S, n_tokens)
-    kw = dict(act=wl.act, alpha=wl.alpha, beta=wl.beta, limit=wl.limit)
+    kw = dict(act=wl.act, alpha=wl.alpha, beta=wl.beta, limit=wl.limit, act_fmt=act_fmt)
     info = threadpoolctl.threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
     t0 = time.perf_counter()
@@ -308,12 +310,16 @@ def main():
     B.lib()  # fail loudly when the HIP library is missing
     dev = torch.device("cuda:0")
     wl = synth.workload(args.workload)
+    if args.act_fmt != "bf16" and wl.wfmt != "mxfp4":
+        print(f"bench.py: --act-fmt {args.act_fmt} needs MXFP4 weights (workload {wl.name} has {wl.wfmt})",
+              file=sys.stderr)
+        sys.exit(2)
     if wl.pregrouped:
         return bench_pregrouped(args, wl, dev)
     print(f"[bench] workload {wl.name}: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.k} {wl.wfmt}", file=sys.stderr,
           flush=True)
     x, ids_d, w_d, W, S, ids, w = make_inputs(wl, dev)
-    p = B.problem(wl.T, wl.H, wl.I, wl.E, wl.k, wl.wfmt, wl.act, wl.alpha, wl.beta, wl.limit)
+    p = B.problem(wl.T, wl.H, wl.I, wl.E, wl.k, wl.wfmt, wl.act, wl.alpha, wl.beta, wl.limit, act_fmt=args.act_fmt)
     ws = B.alloc_workspace(B.moe_experts_workspace_bytes(p), dev)
     out = torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
@@ -378,15 +384,18 @@ def main():
         g1_bytes = n_touched * 2 * wl.H * wl.I * (0.5 + 1 / 32)
         achieved = g1_bytes / (avg["gemm1"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic(wl.name, wl.wfmt),
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                # the committed counters were taken with bf16 activations
+                "traffic": counter_traffic(wl.name, wl.wfmt) if args.act_fmt == "bf16" else None,
                 "kernel": "gemm1 (gate+up, MXFP4)", "algorithmic_bytes": g1_bytes}
 
     res = {
         "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if wl.wfmt == "bf16" else "mxfp4-weights/bf16-act", "data": "synthetic",
+        "dtype": "bf16" if wl.wfmt == "bf16" else f"mxfp4-weights/{args.act_fmt}-act", "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "top_k": wl.k,
-                   "weights": wl.wfmt, "activation": wl.act, "routed_rows": M, "touched_experts": n_touched},
+                   "weights": wl.wfmt, "activation": wl.act, "routed_rows": M, "touched_experts": n_touched,
+                   **({"activations": args.act_fmt} if args.act_fmt != "bf16" else {})},
         "stage_ms": {s: round(v, 4) for s, v in avg.items()},
         "event_ms_per_step": round(float(np.mean(step_ms)), 4),
         "instrumented_ms_per_step": round(instr_ms, 4),
@@ -401,7 +410,7 @@ def main():
                          "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "bound": "hbm"}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, x, ids, w, W, S, args.cpu_sample_tokens)
+        res["cpu_baseline"] = cpu_baseline(wl, x, ids, w, W, S, args.cpu_sample_tokens, args.act_fmt)
     print(json.dumps(res), flush=True)
 
 

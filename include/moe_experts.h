@@ -78,6 +78,18 @@ typedef enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1 } moe_wfmt;
  *   f = alpha * tanh(g / alpha) * sigmoid(g) * beta * tanh(u / beta), alpha > 0, beta > 0. */
 typedef enum { MOE_ACT_SILU = 0, MOE_ACT_SWIGLU_OAI = 1, MOE_ACT_SITU = 2 } moe_act;
 
+/* Activation format of the GEMM inputs. trtllm_mxfp4_moe page,
+ * TrtLlmMxfp4ExpertsBase._supports_quant_scheme: with MXFP4 weights the
+ * activations are either unquantized or dynamically quantized MXFP8.
+ *   MOE_A_BF16:  bf16 rows, carried exactly into the block-scaled MFMA (MXFP4
+ *                weights) as two e4m3 parts per value.
+ *   MOE_A_MXFP8: each GEMM input row (the token rows for GEMM1, the activation
+ *                rows for GEMM2) is quantized per 32 values along K, OCP
+ *                Microscaling v1.0 reading: scale 2^(floor(log2 amax) - 8), its
+ *                e8m0 code clamped to [0, 254]; elements e4m3, round to nearest
+ *                even, saturated at +-448. MXFP4 weights only (else MOE_ENOTSUP). */
+typedef enum { MOE_A_BF16 = 0, MOE_A_MXFP8 = 1 } moe_afmt;
+
 typedef struct {
   int32_t T;     /* tokens: rows of x and out (NvS for the pre-grouped entry) */
   int32_t H;     /* hidden size (K of GEMM1, N of GEMM2); multiple of 64 */
@@ -95,6 +107,7 @@ typedef struct {
                               not weighted (moonep_experts page, MoonEPExperts.apply,
                               input-weighted top-1 routing). Costs one more read and
                               write of the routed rows. */
+  int32_t a_fmt;           /* moe_afmt; 0 (bf16) when zero-initialised */
 } moe_problem;
 
 /* Byte offsets of the intermediates inside a forward workspace (for tests and
@@ -112,6 +125,14 @@ typedef struct {
                         the device to fill the compute units; 1 on the decode path),
                         partial sums per range, added by the combine */
   size_t total;      /* = moe_experts_workspace_bytes() */
+  /* MXFP4 weights only (0 otherwise): GEMM input rows split for the
+   * block-scaled MFMA, each region R rows of K bytes of e4m3 hi parts, then R
+   * rows of K bytes of lo parts (unused with MXFP8 activations), then R rows of
+   * e8m0 scale codes, one per 32 values, padded to a multiple of 16 bytes. */
+  size_t xq;         /* token rows, K = H: R = xq_rows */
+  size_t xq_rows;    /* T when split in token order (small problems, weight on the
+                        activation), else T*k in sorted row order */
+  size_t aq;         /* activation rows, K = I, R = T*k, sorted row order */
 } moe_ws_layout;
 
 /* Workspace bytes a moe_experts_forward call on problem *p needs (0 if *p is

@@ -22,6 +22,8 @@ MOE_ACT_SILU, MOE_ACT_SWIGLU_OAI, MOE_ACT_SITU = 0, 1, 2
 
 _ACT = {"silu": MOE_ACT_SILU, "swiglu_oai": MOE_ACT_SWIGLU_OAI, "situ": MOE_ACT_SITU}
 _WFMT = {"bf16": MOE_W_BF16, "mxfp4": MOE_W_MXFP4}
+MOE_A_BF16, MOE_A_MXFP8 = 0, 1
+_AFMT = {"bf16": MOE_A_BF16, "mxfp8": MOE_A_MXFP8}
 
 EXPORTED = (
     "moe_experts_workspace_bytes", "moe_experts_workspace_layout", "moe_experts_forward",
@@ -37,7 +39,7 @@ class MoeProblem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("wfmt", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
-                ("limit", ctypes.c_float), ("weight_on_input", ctypes.c_int32)]
+                ("limit", ctypes.c_float), ("weight_on_input", ctypes.c_int32), ("a_fmt", ctypes.c_int32)]
 
 
 class MoeRouteProblem(ctypes.Structure):
@@ -48,7 +50,8 @@ class MoeRouteProblem(ctypes.Structure):
 
 class MoeWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("status", "counts", "cu_seqlens", "perm", "inv_perm", "w_sorted", "act", "y", "total")]
+                ("status", "counts", "cu_seqlens", "perm", "inv_perm", "w_sorted", "act", "y", "total",
+                 "xq", "xq_rows", "aq")]
 
 
 class MoeError(RuntimeError):
@@ -104,10 +107,10 @@ def strerror(status: int) -> str:
 
 
 def problem(T, H, I, E, k=1, wfmt="bf16", act="silu", alpha=1.0, beta=0.0, limit=math.inf,
-            weight_on_input=False) -> MoeProblem:
+            weight_on_input=False, act_fmt="bf16") -> MoeProblem:
     return MoeProblem(int(T), int(H), int(I), int(E), int(k), _WFMT[wfmt] if isinstance(wfmt, str) else int(wfmt),
                       _ACT[act] if isinstance(act, str) else int(act), float(alpha), float(beta), float(limit),
-                      int(weight_on_input))
+                      int(weight_on_input), _AFMT[act_fmt] if isinstance(act_fmt, str) else int(act_fmt))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -206,14 +209,15 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def experts_forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, scales=None, act="silu", alpha=1.0, beta=0.0,
-                    limit=math.inf, out=None, workspace=None, weight_on_input=False) -> torch.Tensor:
+                    limit=math.inf, out=None, workspace=None, weight_on_input=False,
+                    act_fmt="bf16") -> torch.Tensor:
     """Token-major experts step on torch tensors; allocates out/workspace if not given."""
     T, H = x.shape
     k = topk_ids.shape[1]
     E = w_gate.shape[0]
     wfmt = "mxfp4" if w_gate.dtype == torch.uint8 else "bf16"
     I = w_gate.shape[1]
-    p = problem(T, H, I, E, k, wfmt, act, alpha, beta, limit, weight_on_input)
+    p = problem(T, H, I, E, k, wfmt, act, alpha, beta, limit, weight_on_input, act_fmt)
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
     if workspace is None:
@@ -225,12 +229,13 @@ def experts_forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, scales=None
 
 
 def experts_forward_grouped(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, scales=None, act="silu", alpha=1.0,
-                            beta=0.0, limit=math.inf, out=None, workspace=None, weight_on_input=False) -> torch.Tensor:
+                            beta=0.0, limit=math.inf, out=None, workspace=None, weight_on_input=False,
+                            act_fmt="bf16") -> torch.Tensor:
     NvS, H = x_nvs.shape
     G = w_gate.shape[0]
     I = w_gate.shape[1]
     wfmt = "mxfp4" if w_gate.dtype == torch.uint8 else "bf16"
-    p = problem(NvS, H, I, G, 1, wfmt, act, alpha, beta, limit, weight_on_input)
+    p = problem(NvS, H, I, G, 1, wfmt, act, alpha, beta, limit, weight_on_input, act_fmt)
     if out is None:
         out = torch.empty(NvS, H, dtype=torch.bfloat16, device=x_nvs.device)
     if workspace is None:

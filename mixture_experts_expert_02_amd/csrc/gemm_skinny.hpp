@@ -105,8 +105,17 @@ struct Params {
   ActParams act;
 };
 
+__device__ __forceinline__ float sat448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
+
 // Split row r of q from bf16 source row sr (256 threads, one 32-value block
 // per thread and step).
+// MX8: MXFP8 activations instead (trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsBase:
+// MXFP4 weights with dynamically quantized MXFP8 activations; OCP
+// Microscaling v1.0 reading): the block's scale is 2^(e - 8) for
+// 2^e <= amax < 2^(e+1) (8 = the largest e4m3 exponent), each scaled value is
+// rounded to e4m3 (to nearest, ties to even) after clamping to +-448 (so it
+// saturates), and there is no lo part.
+template <bool MX8 = false>
 __device__ __forceinline__ void quant_row(const uint16_t* __restrict__ src, size_t sr, int r, int K, const QRows& q) {
   const int KB = K / 32;
   for (int b = threadIdx.x; b < q.sc_stride; b += 256) {
@@ -124,9 +133,26 @@ __device__ __forceinline__ void quant_row(const uint16_t* __restrict__ src, size
     uint32_t mx = 0;  // largest magnitude, as bf16 bits
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = max(mx, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
-    const int code = min(max((int)((mx >> 7) & 0xffu) - 7, 0), 254);
+    const int code = min(max((int)((mx >> 7) & 0xffu) - (MX8 ? 8 : 7), 0), 254);
     const float inv = __uint_as_float((uint32_t)(254 - code) << 23);  // 2^(127 - code), normal for code <= 247
     uint32_t hi[8], lo[8];
+    if (MX8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v0 = sat448(bf16_bits_to_f32(w[2 * i] & 0xffffu) * inv);
+        const float v1 = sat448(bf16_bits_to_f32(w[2 * i] >> 16) * inv);
+        const float v2 = sat448(bf16_bits_to_f32(w[2 * i + 1] & 0xffffu) * inv);
+        const float v3 = sat448(bf16_bits_to_f32(w[2 * i + 1] >> 16) * inv);
+        int h = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+        h = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, h, true);
+        hi[i] = (uint32_t)h;
+      }
+      u32x4* ho = (u32x4*)(q.hi + (size_t)r * K + 32 * b);
+      ho[0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      ho[1] = u32x4{hi[4], hi[5], hi[6], hi[7]};
+      q.sc[(size_t)r * q.sc_stride + b] = (uint8_t)code;
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float v0 = bf16_bits_to_f32(w[2 * i] & 0xffffu) * inv, v1 = bf16_bits_to_f32(w[2 * i] >> 16) * inv;
@@ -152,11 +178,12 @@ __device__ __forceinline__ void quant_row(const uint16_t* __restrict__ src, size
 // One workgroup per row. With perm, output row r is source row perm[r] / div
 // (sorted row -> token), for the first status[1] rows (the valid sorted rows;
 // the rest are never read).
+template <bool MX8>
 __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ src, int rows, int K, QRows q,
                                                     const int32_t* perm, int div, const int32_t* status) {
   const int r = blockIdx.x;
   if (r >= rows || (perm && r >= status[1])) return;
-  quant_row(src, perm ? (size_t)(perm[r] / div) : (size_t)r, r, K, q);
+  quant_row<MX8>(src, perm ? (size_t)(perm[r] / div) : (size_t)r, r, K, q);
 }
 
 template <int FMT>
@@ -222,7 +249,9 @@ __device__ __forceinline__ void lds_barrier() {
 extern __shared__ __attribute__((aligned(16))) uint8_t skinny_scales[];
 
 // SPT: scale pieces per thread (MXFP4; 0 for bf16), scale_pieces_per_thread(K).
-template <int FMT, bool GATED, int SPT>
+// A8: MXFP8 activations (MXFP4 weights): the rows hold one e4m3 part, so each
+// step runs one block-scaled MFMA per stream and loads no lo bytes.
+template <int FMT, bool GATED, int SPT, bool A8 = false>
 __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
   using C = Cfg<FMT>;
   __shared__ __attribute__((aligned(16))) uint8_t sbuf[2][C::BUF_BYTES];
@@ -340,7 +369,7 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
       if (a_live[j]) {
         if (QA) {
           ar.v[j] = *(const u32x4*)(p.Aq.hi + a_row[j] * K + kc);
-          ar.l[j] = *(const u32x4*)(p.Aq.lo + a_row[j] * K + kc);
+          if (!A8) ar.l[j] = *(const u32x4*)(p.Aq.lo + a_row[j] * K + kc);
         } else {
           ar.v[j] = *(const u32x4*)(p.A + a_row[j] * K + kc);
         }
@@ -353,7 +382,7 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       *(u32x4*)&sbuf[buf][a_lds[j]] = ar.v[j] & m;
-      if (QA) *(u32x4*)&sbuf[buf][BM * C::QROW + a_lds[j]] = ar.l[j] & m;
+      if (QA && !A8) *(u32x4*)&sbuf[buf][BM * C::QROW + a_lds[j]] = ar.l[j] & m;
     }
     if (QA && tid < 16) *(u32x4*)&sbuf[buf][2 * BM * C::QROW + 16 * tid] = ar.s;
   };
@@ -406,8 +435,11 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
         const int kbc = min(4 * (c * C::SPC + u) + q, KB - 1);
         const u32x4 h0 = *(const u32x4*)(hrow + 128 * u + 16 * q);
         const u32x4 h1 = *(const u32x4*)(hrow + 128 * u + 64 + 16 * q);
-        const u32x4 l0 = *(const u32x4*)(lrow + 128 * u + 16 * q);
-        const u32x4 l1 = *(const u32x4*)(lrow + 128 * u + 64 + 16 * q);
+        u32x4 l0 = {0u, 0u, 0u, 0u}, l1 = {0u, 0u, 0u, 0u};
+        if (!A8) {
+          l0 = *(const u32x4*)(lrow + 128 * u + 16 * q);
+          l1 = *(const u32x4*)(lrow + 128 * u + 64 + 16 * q);
+        }
         const i32x8 ah = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
         const i32x8 al = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
         const int sa = srow[4 * u + q];
@@ -418,8 +450,10 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
         const i32x8 b1 = {(int)c1w[0], (int)c1w[1], (int)c1w[2], (int)c1w[3], 0, 0, 0, 0};
         acc0 = mfma_fp8_fp4(ah, b0, acc0, sa, sb0);
         acc1 = mfma_fp8_fp4(ah, b1, acc1, sa, sb1);
-        acc0 = mfma_fp8_fp4(al, b0, acc0, sa, sb0);
-        acc1 = mfma_fp8_fp4(al, b1, acc1, sa, sb1);
+        if (!A8) {
+          acc0 = mfma_fp8_fp4(al, b0, acc0, sa, sb0);
+          acc1 = mfma_fp8_fp4(al, b1, acc1, sa, sb1);
+        }
       }
     } else {
       const uint16_t* arow = (const uint16_t*)&sbuf[buf][(l16 * C::LROW + 32 * q) * 2];

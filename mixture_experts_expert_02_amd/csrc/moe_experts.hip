@@ -75,6 +75,8 @@ int check_problem(const moe_problem* p, bool grouped) {
     if (!(p->alpha > 0.f) || !(p->beta > 0.f)) return MOE_ENOTSUP;
   }
   if (p->weight_on_input != 0 && p->weight_on_input != 1) return MOE_EINVAL;
+  if (p->a_fmt != MOE_A_BF16 && p->a_fmt != MOE_A_MXFP8) return MOE_EINVAL;
+  if (p->a_fmt == MOE_A_MXFP8 && p->wfmt != MOE_W_MXFP4) return MOE_ENOTSUP;  // block-scaled MFMA path only
   if (p->H % 64 || p->I % 64) return MOE_ENOTSUP;
   if (p->wfmt == MOE_W_MXFP4 && (p->H > moe::skinny::kMaxMxfp4K || p->I > moe::skinny::kMaxMxfp4K))
     return MOE_ENOTSUP;
@@ -176,11 +178,16 @@ moe::skinny::QRows quant_rows_at(void* base, size_t off, long long R, int K) {
 
 // Split R activation rows; with perm, row r comes from source row perm[r] / div
 // (the first status[1] rows).
-int launch_quant(const void* src, long long R, int K, const moe::skinny::QRows& q, hipStream_t s,
+// (mx8: as MXFP8 activations, one e4m3 part per value).
+int launch_quant(bool mx8, const void* src, long long R, int K, const moe::skinny::QRows& q, hipStream_t s,
                  const int32_t* perm = nullptr, int div = 1, const int32_t* status = nullptr) {
   if (R <= 0) return MOE_OK;
-  hipLaunchKernelGGL(moe::skinny::k_quant_rows, dim3((unsigned)R), dim3(256), 0, s, (const uint16_t*)src, (int)R, K, q,
-                     perm, div, status);
+  if (mx8)
+    hipLaunchKernelGGL(moe::skinny::k_quant_rows<true>, dim3((unsigned)R), dim3(256), 0, s, (const uint16_t*)src,
+                       (int)R, K, q, perm, div, status);
+  else
+    hipLaunchKernelGGL(moe::skinny::k_quant_rows<false>, dim3((unsigned)R), dim3(256), 0, s, (const uint16_t*)src,
+                       (int)R, K, q, perm, div, status);
   return MOE_OK;
 }
 
@@ -262,6 +269,12 @@ int set_attrs() {
       (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 4>,
       (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 8>,
       (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 16>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, true, 4, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, true, 8, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, true, 16, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 4, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 8, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 16, true>,
   };
   for (const void* f : mx)
     if (e == hipSuccess)
@@ -321,7 +334,14 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     using moe::skinny::k_gemm;
     using moe::skinny::W_BF16;
     using moe::skinny::W_MXFP4;
-    if (p.wfmt == MOE_W_MXFP4) {
+    if (p.wfmt == MOE_W_MXFP4 && p.a_fmt == MOE_A_MXFP8) {
+      const size_t lds = moe::skinny::scale_lds_bytes(io.K);
+      switch (moe::skinny::scale_pieces_per_thread(io.K)) {
+        case 4: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 4, true>), grid, block, lds, s, q); break;
+        case 8: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 8, true>), grid, block, lds, s, q); break;
+        default: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 16, true>), grid, block, lds, s, q); break;
+      }
+    } else if (p.wfmt == MOE_W_MXFP4) {
       const size_t lds = moe::skinny::scale_lds_bytes(io.K);
       switch (moe::skinny::scale_pieces_per_thread(io.K)) {
         case 4: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 4>), grid, block, lds, s, q); break;
@@ -403,15 +423,21 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
   const int M = (int)pl.M;
 
   const bool mx = p->wfmt == MOE_W_MXFP4;
+  const bool mx8 = p->a_fmt == MOE_A_MXFP8;
   // MXFP4 with the one-workgroup align: x split in token order in the same
   // launch (GEMM1 reads it through the permutation)
   const bool mx_prologue = mx && pl.fused_align && !p->weight_on_input;
   mark(0);
   if (mx_prologue) {
     const size_t lds = (size_t)(7 * p->E + 16) * 4;
-    hipLaunchKernelGGL(moe::k_align_fused_quant, dim3((unsigned)p->T + 1), dim3(256), lds, s, ids, tw, M, p->E,
-                       bits_for(p->E), pl.BM, o, (const uint16_t*)x, p->T, p->H,
-                       quant_rows_at(ws, pl.xq, p->T, p->H));
+    if (mx8)
+      hipLaunchKernelGGL(moe::k_align_fused_quant<true>, dim3((unsigned)p->T + 1), dim3(256), lds, s, ids, tw, M,
+                         p->E, bits_for(p->E), pl.BM, o, (const uint16_t*)x, p->T, p->H,
+                         quant_rows_at(ws, pl.xq, p->T, p->H));
+    else
+      hipLaunchKernelGGL(moe::k_align_fused_quant<false>, dim3((unsigned)p->T + 1), dim3(256), lds, s, ids, tw, M,
+                         p->E, bits_for(p->E), pl.BM, o, (const uint16_t*)x, p->T, p->H,
+                         quant_rows_at(ws, pl.xq, p->T, p->H));
     if ((rc = launch_status())) return rc;
   } else if ((rc = launch_align(ids, tw, M, p->E, pl.BM, pl, o, ws, s))) {
     return rc;
@@ -435,8 +461,8 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
                        (const int32_t*)o.perm, p->k, (const float*)o.w_sorted, (const int32_t*)o.status, M, p->H,
                        at<uint16_t>(ws, pl.xs));
   if (mx && !mx_prologue) {
-    if (p->weight_on_input) launch_quant(g1.A, pl.M, p->H, g1.Aq, s);
-    else launch_quant(x, pl.M, p->H, g1.Aq, s, o.perm, p->k, o.status);
+    if (p->weight_on_input) launch_quant(mx8, g1.A, pl.M, p->H, g1.Aq, s);
+    else launch_quant(mx8, x, pl.M, p->H, g1.Aq, s, o.perm, p->k, o.status);
   }
   if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
 
@@ -445,7 +471,7 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
             pl.s_cap, y_split, {}};
   if (mx) g2.Aq = quant_rows_at(ws, pl.aq, pl.M, p->I);
   mark(2);
-  if (mx) launch_quant(g2.A, pl.M, p->I, g2.Aq, s);
+  if (mx) launch_quant(mx8, g2.A, pl.M, p->I, g2.Aq, s);
   if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
 
   mark(3);
@@ -478,6 +504,9 @@ int moe_experts_workspace_layout(const moe_problem* p, moe_ws_layout* l) {
   l->act = pl.act;
   l->y = pl.y;
   l->total = pl.total;
+  l->xq = pl.xq;
+  l->xq_rows = pl.xq ? (size_t)(pl.fused_align && !p->weight_on_input ? p->T : pl.M) : 0;
+  l->aq = pl.aq;
   return MOE_OK;
 }
 
@@ -562,6 +591,7 @@ int grouped_impl(const moe_problem* p, const void* x_nvs, const int32_t* cu_seql
   if (p->T == 0) return MOE_OK;
   const Plan pl = make_plan(*p, true);
   if (workspace_bytes < pl.total) return MOE_ENOSPC;
+  if ((rc = set_attrs())) return rc;
   auto mark = [&](int i) {
     if (n_ev) hipEventRecord((hipEvent_t)ev[i], s);
   };
@@ -578,6 +608,7 @@ int grouped_impl(const moe_problem* p, const void* x_nvs, const int32_t* cu_seql
                      p->T, pl.BM, o);
   if ((rc = launch_status())) return rc;
   const bool mx = p->wfmt == MOE_W_MXFP4;
+  const bool mx8 = p->a_fmt == MOE_A_MXFP8;
   GemmIO g1{x_nvs, nullptr, 1, w_gate, w_up, s_gate, s_up, p->I, p->H, at<void>(ws, pl.act), route_w, 1, 0, {}};
   if (p->weight_on_input) {
     g1.A = at<void>(ws, pl.xs);
@@ -589,14 +620,14 @@ int grouped_impl(const moe_problem* p, const void* x_nvs, const int32_t* cu_seql
   mark(1);
   if (mx) {
     g1.Aq = quant_rows_at(ws, pl.xq, pl.M, p->H);
-    launch_quant(g1.A, pl.M, p->H, g1.Aq, s);
+    launch_quant(mx8, g1.A, pl.M, p->H, g1.Aq, s);
   }
   if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
   GemmIO g2{at<void>(ws, pl.act), nullptr, 1, w_down, nullptr, s_down, nullptr, p->H, p->I, out_nvs, nullptr, 1, 0, {}};
   mark(2);
   if (mx) {
     g2.Aq = quant_rows_at(ws, pl.aq, pl.M, p->I);
-    launch_quant(g2.A, pl.M, p->I, g2.Aq, s);
+    launch_quant(mx8, g2.A, pl.M, p->I, g2.Aq, s);
   }
   if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
   mark(3);

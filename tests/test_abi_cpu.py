@@ -215,3 +215,13 @@ def test_grouped_timed_event_count_checked():
     ev = (ctypes.c_void_p * 3)()
     assert L.moe_experts_forward_grouped_timed(ctypes.byref(g), fake, fake, fake, fake, fake, fake, None, None, None,
                                                fake, fake, 1 << 40, None, ev, 3) == B.MOE_EINVAL
+
+
+def test_mxfp8_activations_need_mxfp4_weights():
+    # checked on the host: no device needed
+    ok = B.problem(32, 256, 256, 8, 2, wfmt="mxfp4", act_fmt="mxfp8")
+    assert B.moe_experts_workspace_bytes(ok) > 0
+    assert B.moe_experts_workspace_bytes(B.problem(32, 256, 256, 8, 2, wfmt="bf16", act_fmt="mxfp8")) == 0
+    assert B.moe_experts_workspace_bytes(B.problem(32, 256, 256, 8, 2, wfmt="mxfp4", act_fmt=7)) == 0
+    lay = B.moe_experts_workspace_layout(ok)
+    assert lay.xq > 0 and lay.aq > lay.xq and lay.xq_rows == 32

@@ -137,7 +137,7 @@ def kernel_source_hash(wfmt: str) -> str:
 
 def counter_traffic(workload: str, wfmt: str):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary
-    of this workload: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled
+    of this workload (name suffixed _mxfp8 for MXFP8 activations): FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled
     by what the same counter read for a 1 GiB device copy. None when there is
     no summary or the GEMM sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"gemm1_{workload}_counters.txt")
@@ -385,8 +385,8 @@ def main():
         achieved = g1_bytes / (avg["gemm1"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4),
-                # the committed counters were taken with bf16 activations
-                "traffic": counter_traffic(wl.name, wl.wfmt) if args.act_fmt == "bf16" else None,
+                "traffic": counter_traffic(wl.name + ("" if args.act_fmt == "bf16" else "_" + args.act_fmt),
+                                           wl.wfmt),
                 "kernel": "gemm1 (gate+up, MXFP4)", "algorithmic_bytes": g1_bytes}
 
     res = {

@@ -22,18 +22,20 @@ struct SplitSum {
   int64_t stride;         // elements between partial outputs
 };
 
-// One workgroup per token; each thread sums 8 consecutive columns, slot j
-// outer and K range s inner, both ascending. The (j, s) rows are fetched
-// eight at a time before any is added, so a thread has up to eight loads in
-// flight instead of one; the additions keep the order above.
+// One workgroup per token and 2048 columns (blockIdx.y); each thread sums 8
+// consecutive columns, slot j outer and K range s inner, both ascending. The
+// (j, s) rows are fetched eight at a time before any is added, so a thread
+// has up to eight loads in flight instead of one; the additions keep the
+// order above.
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* y, const int32_t* inv_perm, int T, int k,
                                                  int H, const SplitSum ss, uint16_t* out) {
   const int t = blockIdx.x;
   if (t >= T) return;
+  const int h0 = blockIdx.y * 256 * 8;
   const int S = ss.s_cap > 1 ? split_k_count(ss.status[2] * ss.n_tiles, ss.kt, ss.ncu, ss.s_cap) : 1;
   const int n = k * S;  // (j, s) pairs, j-major
   const int32_t* ip = inv_perm + (size_t)t * k;
-  for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
+  for (int h = h0 + threadIdx.x * 8; h < min(H, h0 + 256 * 8); h += 256 * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int base = 0; base < n; base += 8) {
       u32x4 v[8];

@@ -477,7 +477,7 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
   mark(3);
   moe::SplitSum ss{o.status, ceil_div(p->H, moe::big::BN), p->I / moe::big::BK, 1, pl.s_cap, y_split};
   if (pl.s_cap > 1 && (rc = device_cus(&ss.ncu))) return rc;
-  hipLaunchKernelGGL(moe::k_combine, dim3(p->T), dim3(256), 0, s, at<const uint16_t>(ws, pl.y),
+  hipLaunchKernelGGL(moe::k_combine, dim3(p->T, ceil_div(p->H, 256 * 8)), dim3(256), 0, s, at<const uint16_t>(ws, pl.y),
                      (const int32_t*)o.inv_perm, p->T, p->k, p->H, ss, (uint16_t*)out);
   mark(4);
   return launch_status();

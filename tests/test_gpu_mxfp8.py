@@ -83,6 +83,10 @@ CASES = [
     ("weight_on_input", (13, 192, 128, 5, 1), "silu", {"on_input": True}),
     ("sorted_split_chunked", (2100, 128, 256, 4, 2), "swiglu_oai", {"masked": 0.05}),
     ("k8192", (4, 8192, 256, 3, 2), "swiglu_oai", {}),
+    ("one_token", (1, 256, 320, 6, 3), "silu", {}),
+    ("k16384_down", (3, 256, 16384, 2, 1), "silu", {}),   # GEMM2's K at the 16384 limit
+    ("masked_bad", (20, 128, 192, 4, 2), "silu", {"masked": 0.5, "bad": 0.1}),
+    ("situ", (9, 256, 320, 6, 3), "situ", {}),
 ]
 
 
@@ -107,6 +111,8 @@ def test_mxfp8_forward_matches_oracle(name, shape, act, extra):
     assert err <= TOL
     again = run_gpu(x, ids, w, W, S, act_kw)
     assert torch.equal(out, again)
+    dead = np.all((ids < 0) | (ids >= E), axis=1)
+    assert np.all(got[dead] == 0)
 
 
 def test_mxfp8_pregrouped_matches_oracle():

@@ -88,6 +88,9 @@ def test_workspace_room_for_split_down_projection(monkeypatch):
     (dict(act="situ", alpha=math.inf, beta=1.0), B.MOE_EINVAL),
     (dict(act=3), B.MOE_EINVAL),
     (dict(weight_on_input=2), B.MOE_EINVAL),
+    (dict(act_fmt="mxfp8"), B.MOE_ENOTSUP),        # MXFP8 activations need MXFP4 weights
+    (dict(act_fmt=2), B.MOE_EINVAL),
+    (dict(wfmt="mxfp4", act_fmt=-1), B.MOE_EINVAL),
 ])
 def test_invalid_problems_rejected(kw, code):
     base = dict(T=16, H=128, I=256, E=8, k=2)

@@ -44,6 +44,12 @@ Readings where the pages are silent:
     are bf16; the scheme quantizes them dynamically), so a row computed here
     in float64 is rounded to bf16 (to nearest even) first.
 
+Parity unpinned (the pages give a name and parameters but no formula, so the
+pins check this code against the reading, not against the pages): the
+SwiGLU-OAI formula, and the choice of the OCP MX scale and rounding rule for
+MXFP8 activations. The e2m1 and e4m3 encodings themselves are pinned
+exhaustively.
+
 Everything is computed in float64 from exactly widened inputs.
 """
 from __future__ import annotations

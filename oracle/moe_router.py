@@ -11,7 +11,10 @@ Sources (the vLLM API pages this follows):
     correction bias, the number of expert groups, the number of groups kept
     (topk_group) and a routed scaling factor.
 
-The pages name these methods and parameters but print no formula. Readings:
+The pages name these methods and parameters but print no formula, so parity
+is unpinned for the formulas themselves: the pins check this code against the
+readings below (and against scipy's softmax and expit), not against the
+pages. Readings:
   * Renormalize / RenormalizeNaive: probabilities p = softmax(logits) over all
     experts, the k largest kept, divided by their sum. The two names differ
     only in evaluation order (top-k of the logits then a softmax over the k

@@ -1,22 +1,28 @@
 """Benchmark of the MoE experts step on one MI355X.
 
-A step is one full experts pass (align, GEMM1 + activation, GEMM2, combine)
-over one batch of synthetic, seeded input resident in HBM. Prints one JSON
-line. Default workload: the Mixtral-shaped prefill layer (T=4096, H=4096,
-I=14336, E=8, top-2, bf16), reported in TFLOP/s of routed-row GEMM work.
+A step is one full experts pass (align, GEMM1 + activation, GEMM2, combine;
+for the pre-grouped layout: segment tables, GEMM1, GEMM2, zero tail) over one
+batch of synthetic, seeded input resident in HBM. Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--calib-copy] [--router]
+The metric has two halves: bf16 prefill TFLOP/s and MXFP4 decode weight-stream
+GB/s. The default run (--workload all) measures four workloads one after the
+other and puts the headline on the largest, the fine-grained prefill layer
+(T=8192, H=7168, I=2048, E=256 resident experts, top-8, Zipf-skewed load);
+the Mixtral-shaped prefill, the MXFP4 decode step and the pre-grouped layout
+go into the same line under "configs", each with its step time, value,
+roofline and CPU-oracle baseline.
 
---workload pregrouped times the pre-grouped entry (segments already
-contiguous, caller's cu_seqlens) instead of the token-major step.
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|NAME]
+                  [--no-cpu-baseline] [--calib-copy] [--router] [--act-fmt bf16|mxfp8]
+                  [--weight-copies N]
 
-The K timed steps run twice after the warm-up: first with hipEvents that the
-library records between its launches on the benchmark's stream
-(moe_experts_forward_timed), which give the per-kernel times (stage_ms, the
-roofline's kernel time) and the instrumented pass's own wall-clock time,
-then with no instrumentation: that pass's wall-clock time gives ms_per_step
-and value.
+The K timed steps of a workload run twice after the warm-up: first with
+hipEvents that the library records between its launches on the benchmark's
+stream (the *_timed entry points), which give the per-kernel times (stage_ms,
+the roofline's kernel time), then with no instrumentation: that pass's
+wall-clock time gives ms_per_step and value. Decode steps rotate over several
+copies of the weights (--weight-copies, default 4, 6.8 GB in all), so that
+the 256 MB Infinity Cache cannot serve one step's weights to the next.
 """
 from __future__ import annotations
 
@@ -34,26 +40,39 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 STAGES = ("align", "gemm1", "gemm2", "combine")
 METRIC = "MoE experts TFLOP/s (bf16 prefill) + weight-stream GB/s (MXFP4 decode), 1 GPU"
+HEADLINE = "fine_grained_prefill"
+NESTED = ("mixtral_prefill", "mxfp4_decode", "pregrouped")
+DECODE_MIN_STEPS = 200      # a 0.2 ms step: fewer steps let the timed region's ends show
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 20; 200 for the MXFP4 decode workload, whose step is 0.25 ms, "
-                         "so that the timed region's fixed start and end cost stays small per step)")
+    ap.add_argument("--steps", type=int, default=20,
+                    help="timed steps of the headline workload (decode workloads time at least "
+                         f"{DECODE_MIN_STEPS}, reported in their own 'steps')")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--workload", default="all",
+                    help="'all' (headline fine_grained_prefill plus nested configs) or one workload name")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None,
+                    help="tokens (rows) of the oracle's sample; default per workload")
     ap.add_argument("--print-source-hash", action="store_true")
     ap.add_argument("--router", action="store_true",
                     help="run the router (moe_route, Renormalize) on the workload's logits inside each step")
     ap.add_argument("--act-fmt", default="bf16", choices=("bf16", "mxfp8"),
                     help="activation format of the GEMM inputs (mxfp8: MXFP4-weight workloads only)")
+    ap.add_argument("--weight-copies", type=int, default=4,
+                    help="MXFP4 decode: copies of the weights the steps rotate over")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
+
+
+# Oracle sample per workload (tokens, or rows of the pre-grouped layout):
+# about 2-8 s of float64 BLAS work on 16 host threads each.
+CPU_SAMPLE = {"fine_grained_prefill": 512, "mixtral_prefill": 1024, "mxfp4_decode": 32, "pregrouped": 1024,
+              "tiny": 64}
 
 
 def timed_passes(step, K, hev, n_ev, extra=None):
@@ -68,12 +87,12 @@ def timed_passes(step, K, hev, n_ev, extra=None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(evs[i], xevs[i])
+        step(i, evs[i], xevs[i])
     torch.cuda.synchronize()
     instr = (time.perf_counter() - t0) * 1e3 / K
     t0 = time.perf_counter()
-    for _ in range(K):
-        step()
+    for i in range(K):
+        step(i)
     torch.cuda.synchronize()
     plain = (time.perf_counter() - t0) * 1e3 / K
     return plain, instr, evs, xevs
@@ -111,19 +130,6 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def make_inputs(wl, dev):
-    import torch
-    import synth
-    ids, w = synth.make_routing(wl)
-    x = synth.make_x(wl, device=dev)
-    if wl.wfmt == "mxfp4":
-        (cg, sg), (cu, su), (cd, sd) = synth.make_mxfp4_weights(wl, device=dev)
-        W, S = (cg, cu, cd), (sg, su, sd)
-    else:
-        W, S = synth.make_bf16_weights(wl, device=dev), (None, None, None)
-    return x, torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev), W, S, ids, w
-
-
 def kernel_source_hash(wfmt: str) -> str:
     """sha256 of the sources the GEMM1 kernel of a weight format is built from
     (bf16: the prefill GEMM; mxfp4: the decode GEMM)."""
@@ -135,12 +141,13 @@ def kernel_source_hash(wfmt: str) -> str:
     return h.hexdigest()
 
 
-def counter_traffic(workload: str, wfmt: str):
+def counter_traffic(name: str, wfmt: str):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary
-    of this workload (name suffixed _mxfp8 for MXFP8 activations): FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled
-    by what the same counter read for a 1 GiB device copy. None when there is
-    no summary or the GEMM sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"gemm1_{workload}_counters.txt")
+    profiles/gemm1_<name>_counters.txt: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter read for a 1 GiB device
+    copy. None when there is no summary or the GEMM sources changed since the
+    counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"gemm1_{name}_counters.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -164,50 +171,59 @@ def touched_weight_bytes(wl, ids):
     return n, n * per
 
 
-def subproblem_host(wl, x, ids, w, W, S, n_tokens):
-    """Host copies of the first n_tokens tokens and of the experts they touch
-    (renumbered 0..E'-1): plain float32 / uint8 numpy arrays for the oracle."""
+def cpu_threads():
+    """(threads the oracle's BLAS runs on, CPUs this process may use, CPUs of the host)."""
+    import threadpoolctl
+    info = threadpoolctl.threadpool_info()
+    blas = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = os.cpu_count() or 1
+    return int(blas), int(aff), int(os.cpu_count() or 1)
+
+
+def cpu_baseline(wl, x, ids, w, W, S, n_tokens, act_fmt="bf16"):
+    """The CPU oracle, as it is, on the first n_tokens tokens of the workload
+    (with the experts they touch, renumbered, copied to the host)."""
     import numpy as np
+    import torch
+    import oracle
     import synth
+    n_tokens = min(n_tokens, wl.T)
     ids_s = ids[:n_tokens]
     touched = sorted({int(e) for e in ids_s.ravel() if 0 <= e < wl.E})
     remap = np.full(wl.E, -1, dtype=np.int32)
     remap[touched] = np.arange(len(touched), dtype=np.int32)
     ids_c = np.where((ids_s >= 0) & (ids_s < wl.E), remap[np.clip(ids_s, 0, wl.E - 1)], -1).astype(np.int32)
     xs = synth.bf16_to_f32(x[:n_tokens])
-    sel = __import__("torch").as_tensor(touched, device=x.device)
+    sel = torch.as_tensor(touched, device=x.device)
     if wl.wfmt == "mxfp4":
-        Wh = [(W[i][sel].cpu().numpy(), S[i][sel].cpu().numpy()) for i in range(3)]
+        Wh = [(W[i].index_select(0, sel).cpu().numpy(), S[i].index_select(0, sel).cpu().numpy()) for i in range(3)]
     else:
-        Wh = [synth.bf16_to_f32(W[i][sel]) for i in range(3)]
-    return xs, ids_c, w[:n_tokens], Wh
-
-
-def cpu_baseline(wl, x, ids, w, W, S, n_tokens, act_fmt="bf16"):
-    """The CPU oracle, as it is, on the first n_tokens tokens of the workload."""
-    import numpy as np
-    import threadpoolctl
-    import oracle
-    n_tokens = min(n_tokens, wl.T)
-    xs, ids_c, ws_, Wh = subproblem_host(wl, x, ids, w, W, S, n_tokens)
+        Wh = [synth.bf16_to_f32(W[i].index_select(0, sel)) for i in range(3)]
     kw = dict(act=wl.act, alpha=wl.alpha, beta=wl.beta, limit=wl.limit, act_fmt=act_fmt)
-    info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    blas, aff, host = cpu_threads()
     t0 = time.perf_counter()
-    oracle.experts_forward(xs, ids_c, ws_, *Wh, **kw)
+    oracle.experts_forward(xs, ids_c, w[:n_tokens], *Wh, **kw)
     dt = time.perf_counter() - t0
-    slots = int(np.sum((ids_c >= 0)))
-    flops = 6.0 * slots * wl.H * wl.I
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {n_tokens} of {wl.T} tokens ({slots} routed slots) of {wl.name}, float64 numpy, "
-                      f"{dt:.1f} s"}
+    slots = int(np.sum(ids_c >= 0))
+    if wl.wfmt == "mxfp4":
+        value = len(touched) * 3 * wl.H * wl.I * (0.5 + 1 / 32) / dt / 1e9
+        unit = "GB/s"
+    else:
+        value = 6.0 * slots * wl.H * wl.I / dt / 1e12
+        unit = "TFLOP/s"
+    return {"value": round(value, 4), "unit": unit, "cores": blas, "kind": "oracle",
+            "sample": f"first {n_tokens} of {wl.T} tokens ({slots} routed slots, {len(touched)} experts) of "
+                      f"{wl.name}, float64 numpy on {blas} BLAS threads, {dt:.1f} s",
+            "cpus_available": aff, "host_cpus": host}
 
 
 def cpu_baseline_pregrouped(wl, x, cu, rw, W, n_rows):
     """The float64 oracle on rows [0, n_rows) of the pre-grouped layout (the
     segments they fall in, with their weights copied to the host)."""
     import numpy as np
-    import threadpoolctl
     import torch
     import oracle
     import synth
@@ -216,17 +232,26 @@ def cpu_baseline_pregrouped(wl, x, cu, rw, W, n_rows):
     xs = synth.bf16_to_f32(x[:n_rows])
     sel = torch.as_tensor(segs, device=x.device)
     Wh = [synth.bf16_to_f32(t.index_select(0, sel)) for t in W]
-    info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    blas, aff, host = cpu_threads()
     t0 = time.perf_counter()
     oracle.pregrouped_forward(xs, sub_cu, rw[:n_rows], *Wh)
     dt = time.perf_counter() - t0
     flops = 6.0 * n_rows * wl.H * wl.I
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {n_rows} of {wl.T} rows ({len(segs)} segments) of {wl.name}, float64 numpy, {dt:.1f} s"}
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": blas, "kind": "oracle",
+            "sample": f"first {n_rows} of {wl.T} rows ({len(segs)} segments) of {wl.name}, float64 numpy on "
+                      f"{blas} BLAS threads, {dt:.1f} s",
+            "cpus_available": aff, "host_cpus": host}
 
 
-def bench_pregrouped(args, wl, dev):
+def _calib_copy(dev):
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    del a, b
+
+
+def run_pregrouped(args, wl, dev, K):
     """The pre-grouped entry (rows already contiguous per weight row, caller's
     cu_seqlens) on the pre-grouped workload: GEMM1, GEMM2 and the zero tail."""
     import numpy as np
@@ -246,21 +271,17 @@ def bench_pregrouped(args, wl, dev):
     stream = torch.cuda.current_stream()
     hev = HipEvents()
 
-    def step(evs=(), _unused=None):
+    def step(i, evs=(), _unused=None):
         rc = B.moe_experts_forward_grouped_timed(p, x, cu_d, rw_d, *W, None, None, None, out, ws, list(evs),
                                                  stream=stream)
         if rc != 0:
             raise B.MoeError(rc, "moe_experts_forward_grouped_timed")
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     if args.calib_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        del a, b
+        _calib_copy(dev)
     torch.cuda.synchronize()
-    K = args.steps if args.steps is not None else 20
     ms_per_step, instr_ms, evs, _ = timed_passes(step, K, hev, 5)
     stages = ("prep", "gemm1", "gemm2", "zero_tail")
     avg = {s: float(np.mean([hev.elapsed_ms(e[j], e[j + 1]) for e in evs])) for j, s in enumerate(stages)}
@@ -276,9 +297,8 @@ def bench_pregrouped(args, wl, dev):
             "kernel": "gemm1 (gate+up, bf16)",
             "algorithmic_bytes": n_touched * 2 * wl.I * wl.H * 2 + M * wl.H * 2 + M * wl.I * 2}
     res = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "steps": K,
+        "ms_per_step": round(ms_per_step, 4), "dtype": "bf16",
         "config": {"workload": wl.name, "NvS": wl.T, "H": wl.H, "I": wl.I, "segments": wl.E, "weights": wl.wfmt,
                    "activation": wl.act, "routed_rows": M, "touched_experts": n_touched},
         "stage_ms": {s: round(v, 4) for s, v in avg.items()},
@@ -287,39 +307,33 @@ def bench_pregrouped(args, wl, dev):
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline_pregrouped(wl, x, cu, rw, W, args.cpu_sample_tokens)
-    print(json.dumps(res), flush=True)
+        print(f"[bench] {wl.name}: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        n = args.cpu_sample_tokens or CPU_SAMPLE[wl.name]
+        res["cpu_baseline"] = cpu_baseline_pregrouped(wl, x, cu, rw, W, n)
+    return res
 
 
-def main():
-    args = parse()
-    if args.print_source_hash:
-        import synth
-        print(kernel_source_hash(synth.WORKLOADS[args.workload].wfmt))
-        return
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the experts step "
-              f"holds every expert on a single MI355X.", file=sys.stderr)
-        sys.exit(2)
+def run_token_major(args, wl, dev, K, act_fmt):
     import numpy as np
     import torch
     import synth
     from mixture_experts_expert_02_amd import binding as B
-
-    B.lib()  # fail loudly when the HIP library is missing
-    dev = torch.device("cuda:0")
-    wl = synth.workload(args.workload)
-    if args.act_fmt != "bf16" and wl.wfmt != "mxfp4":
-        print(f"bench.py: --act-fmt {args.act_fmt} needs MXFP4 weights (workload {wl.name} has {wl.wfmt})",
-              file=sys.stderr)
-        sys.exit(2)
-    if wl.pregrouped:
-        return bench_pregrouped(args, wl, dev)
     print(f"[bench] workload {wl.name}: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.k} {wl.wfmt}", file=sys.stderr,
           flush=True)
-    x, ids_d, w_d, W, S, ids, w = make_inputs(wl, dev)
-    p = B.problem(wl.T, wl.H, wl.I, wl.E, wl.k, wl.wfmt, wl.act, wl.alpha, wl.beta, wl.limit, act_fmt=args.act_fmt)
+    ids, w = synth.make_routing(wl)
+    ids_d, w_d = torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)
+    x = synth.make_x(wl, device=dev)
+    if wl.wfmt == "mxfp4":
+        (cg, sg), (cu, su), (cd, sd) = synth.make_mxfp4_weights(wl, device=dev)
+        W, S = (cg, cu, cd), (sg, su, sd)
+        copies = max(1, args.weight_copies)
+    else:
+        W, S = synth.make_bf16_weights(wl, device=dev), (None, None, None)
+        copies = 1
+    # copy 0 is the generated tensors; the others are clones at other addresses
+    sets = [(W, S)] + [(tuple(t.clone() for t in W), tuple(t.clone() for t in S) if S[0] is not None else S)
+                       for _ in range(copies - 1)]
+    p = B.problem(wl.T, wl.H, wl.I, wl.E, wl.k, wl.wfmt, wl.act, wl.alpha, wl.beta, wl.limit, act_fmt=act_fmt)
     ws = B.alloc_workspace(B.moe_experts_workspace_bytes(p), dev)
     out = torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
@@ -330,27 +344,24 @@ def main():
         logits_d = torch.from_numpy(synth.make_logits(wl)).to(dev)
         rp = B.route_problem(wl.T, wl.E, wl.k, "renormalize")
 
-    def step(evs=(), rev=None):
+    def step(i, evs=(), rev=None):
+        Wi, Si = sets[i % copies]
         if args.router:
             if rev is not None:
                 hev.record(rev, stream)
             rc = B.moe_route(rp, logits_d, None, ids_d, w_d, stream=stream)
             if rc != 0:
                 raise B.MoeError(rc, "moe_route")
-        rc = B.moe_experts_forward_timed(p, x, ids_d, w_d, *W, *S, out, ws, list(evs), stream=stream)
+        rc = B.moe_experts_forward_timed(p, x, ids_d, w_d, *Wi, *Si, out, ws, list(evs), stream=stream)
         if rc != 0:
             raise B.MoeError(rc, "moe_experts_forward_timed")
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     if args.calib_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        del a, b
+        _calib_copy(dev)
     torch.cuda.synchronize()
 
-    K = args.steps if args.steps is not None else (200 if wl.wfmt == "mxfp4" else 20)
     ms_per_step, instr_ms, evs, revs = timed_passes(step, K, hev, 5, extra=args.router)
     stage_ms = {s: [] for s in (("router",) if args.router else ()) + STAGES}
     for e, r in zip(evs, revs):
@@ -368,7 +379,6 @@ def main():
     n_touched, wbytes = touched_weight_bytes(wl, ids)
     avg = {s: float(np.mean(v)) for s, v in stage_ms.items()}
     if wl.wfmt == "bf16":
-        metric = METRIC
         unit = "TFLOP/s"
         value = wl.flops / (ms_per_step * 1e-3) / 1e12
         g1_flops = 4.0 * M * wl.H * wl.I
@@ -378,24 +388,22 @@ def main():
                 "kernel": "gemm1 (gate+up, bf16)",
                 "algorithmic_bytes": n_touched * 2 * wl.I * wl.H * 2 + M * wl.H * 2 + M * wl.I * 2}
     else:
-        metric = METRIC
         unit = "GB/s"
         value = (wbytes + 2 * wl.T * wl.H * 2) / (ms_per_step * 1e-3) / 1e9
         g1_bytes = n_touched * 2 * wl.H * wl.I * (0.5 + 1 / 32)
         achieved = g1_bytes / (avg["gemm1"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": counter_traffic(wl.name + ("" if args.act_fmt == "bf16" else "_" + args.act_fmt),
-                                           wl.wfmt),
+                "traffic": counter_traffic(wl.name + ("" if act_fmt == "bf16" else "_" + act_fmt), wl.wfmt),
                 "kernel": "gemm1 (gate+up, MXFP4)", "algorithmic_bytes": g1_bytes}
-
     res = {
-        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if wl.wfmt == "bf16" else f"mxfp4-weights/{args.act_fmt}-act", "data": "synthetic",
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "steps": K,
+        "ms_per_step": round(ms_per_step, 4),
+        "dtype": "bf16" if wl.wfmt == "bf16" else f"mxfp4-weights/{act_fmt}-act",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "top_k": wl.k,
                    "weights": wl.wfmt, "activation": wl.act, "routed_rows": M, "touched_experts": n_touched,
-                   **({"activations": args.act_fmt} if args.act_fmt != "bf16" else {})},
+                   **({"weight_copies": copies} if copies > 1 else {}),
+                   **({"activations": act_fmt} if act_fmt != "bf16" else {})},
         "stage_ms": {s: round(v, 4) for s, v in avg.items()},
         "event_ms_per_step": round(float(np.mean(step_ms)), 4),
         "instrumented_ms_per_step": round(instr_ms, 4),
@@ -409,9 +417,68 @@ def main():
                          "algorithmic_bytes": rbytes, "achieved": round(gbs, 1), "unit": "GB/s",
                          "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "bound": "hbm"}
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, x, ids, w, W, S, args.cpu_sample_tokens, args.act_fmt)
-    print(json.dumps(res), flush=True)
+        print(f"[bench] {wl.name}: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        n = args.cpu_sample_tokens or CPU_SAMPLE.get(wl.name, 1024)
+        res["cpu_baseline"] = cpu_baseline(wl, x, ids, w, W, S, n, act_fmt)
+    return res
+
+
+def run_one(args, name, dev, K):
+    import gc
+    import torch
+    import synth
+    wl = synth.workload(name)
+    if wl.wfmt == "mxfp4":
+        K = max(K, DECODE_MIN_STEPS)
+    act_fmt = args.act_fmt if wl.wfmt == "mxfp4" else "bf16"
+    res = run_pregrouped(args, wl, dev, K) if wl.pregrouped else run_token_major(args, wl, dev, K, act_fmt)
+    gc.collect()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.print_source_hash:
+        import synth
+        print(kernel_source_hash(synth.WORKLOADS[args.workload].wfmt))
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the experts step "
+              f"holds every expert on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    from mixture_experts_expert_02_amd import binding as B
+
+    B.lib()  # fail loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    names = [HEADLINE, *NESTED] if args.workload == "all" else [args.workload]
+    for n in names:
+        if n not in synth.WORKLOADS:
+            print(f"bench.py: unknown workload {n!r}", file=sys.stderr)
+            sys.exit(2)
+    if args.act_fmt != "bf16" and all(synth.WORKLOADS[n].wfmt != "mxfp4" for n in names):
+        print(f"bench.py: --act-fmt {args.act_fmt} needs an MXFP4-weight workload", file=sys.stderr)
+        sys.exit(2)
+    results = {}
+    for n in names:
+        results[n] = run_one(args, n, dev, args.steps)
+        r = results[n]
+        print(f"[bench] {n}: {r['value']} {r['unit']}, {r['ms_per_step']} ms/step, "
+              f"roofline frac {r['roofline']['frac']}", file=sys.stderr, flush=True)
+    head = results[names[0]]
+    line = {
+        "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1, "steps": head["steps"],
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic",
+        "config": head["config"],
+        **{k: v for k, v in head.items() if k not in ("metric", "value", "unit", "steps", "ms_per_step", "dtype",
+                                                     "config")},
+    }
+    if len(names) > 1:
+        line["configs"] = {n: results[n] for n in names[1:]}
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

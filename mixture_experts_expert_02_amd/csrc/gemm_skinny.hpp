@@ -375,7 +375,9 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
         }
       }
     }
-    if (QA) ar.s = *(const u32x4*)(p.Aq.sc + s_row * p.Aq.sc_stride + 16 * c);
+    // chunks past the last (the loop below loads two ahead) re-read the last
+    // chunk's scale bytes: a row holds exactly 16 * nch of them
+    if (QA) ar.s = *(const u32x4*)(p.Aq.sc + s_row * p.Aq.sc_stride + 16 * min(c, nch - 1));
   };
   auto store_a = [&](const ARegs& ar, int buf, int c) {
     const uint32_t m = c * C::KC + VPP * pc < K ? ~0u : 0u;

@@ -69,3 +69,32 @@ def sampled_token_oracle(x, ids, w, wg, wu, wd, tokens, act_kw=None, mx=False):
 
 def wl_act_kw(wl):
     return dict(act=wl.act, alpha=wl.alpha, beta=wl.beta, limit=wl.limit)
+
+
+class Guarded:
+    """A device byte buffer between two canary bands. `body` is the usable
+    part (256-byte aligned, `nbytes` long); `poison()` fills it with 0xff
+    bytes (bf16 NaN, int32 -1, float32 NaN) and the bands with a fixed
+    pattern; `check_bands()` asserts that the bands still hold it."""
+
+    BAND = 4096
+
+    def __init__(self, nbytes: int, device):
+        self.nbytes = max(int(nbytes), 256)
+        self.full = torch.empty(self.nbytes + 2 * self.BAND, dtype=torch.uint8, device=device)
+        self.body = self.full[self.BAND: self.BAND + self.nbytes]
+        self.pattern = (torch.arange(self.BAND, device=device, dtype=torch.int32) * 37 + 11).to(torch.uint8)
+        self.poison()
+
+    def poison(self):
+        self.body.fill_(0xFF)
+        self.full[: self.BAND].copy_(self.pattern)
+        self.full[self.BAND + self.nbytes:].copy_(self.pattern)
+
+    def check_bands(self):
+        assert torch.equal(self.full[: self.BAND], self.pattern), "write below the buffer"
+        assert torch.equal(self.full[self.BAND + self.nbytes:], self.pattern), "write past the buffer"
+
+    def view_bf16(self, *shape):
+        n = int(np.prod(shape))
+        return self.body[: 2 * n].view(torch.bfloat16).view(*shape)

@@ -185,6 +185,27 @@ int moe_experts_forward_timed(const moe_problem* p, const void* x, const int32_t
                               size_t workspace_bytes, moe_stream_t stream,
                               void* const* stage_events, int n_events);
 
+/*
+ * moe_experts_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The library's own scratch array (32 MiB,
+ * one per device, held from the library's load until the process ends)
+ * serves as the workspace; nothing is allocated or freed, and the call
+ * enqueues the same kernels as moe_experts_forward on `stream`.
+ * Arguments, layouts and results are those of moe_experts_forward.
+ * Limits: problems whose moe_experts_workspace_bytes() exceeds 32 MiB get
+ * MOE_ENOSPC (a decode step of T=32, H=I=2880, E=128, top-4 needs about
+ * 3 MiB). Every call on a device shares that device's scratch and leaves its
+ * contents behind (no kernel expects it to start zeroed): calls that overlap
+ * on one device, on any streams, race. The device status word stays in the
+ * scratch, so bad expert ids are skipped as by moe_experts_forward but not
+ * reported (moe_device_error needs a caller-owned workspace).
+ */
+int moe_experts_forward_noalloc(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                                const float* topk_weights, const void* w_gate, const void* w_up,
+                                const void* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                                const uint8_t* s_down, void* out, moe_stream_t stream);
+
 /* Workspace bytes for moe_align on (T, k, E); 0 if invalid. */
 size_t moe_align_workspace_bytes(int32_t T, int32_t k, int32_t E);
 

@@ -29,7 +29,7 @@ EXPORTED = (
     "moe_experts_workspace_bytes", "moe_experts_workspace_layout", "moe_experts_forward",
     "moe_experts_forward_timed", "moe_align_workspace_bytes", "moe_align",
     "moe_experts_grouped_workspace_bytes", "moe_experts_forward_grouped", "moe_device_error",
-    "moe_strerror", "moe_route", "moe_experts_forward_grouped_timed",
+    "moe_strerror", "moe_route", "moe_experts_forward_grouped_timed", "moe_experts_forward_noalloc",
 )
 MOE_ROUTE_RENORMALIZE, MOE_ROUTE_DEEPSEEK_V3 = 0, 1
 _ROUTE = {"renormalize": MOE_ROUTE_RENORMALIZE, "deepseek_v3": MOE_ROUTE_DEEPSEEK_V3}
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.moe_experts_forward.restype = ctypes.c_int
         L.moe_experts_forward_timed.argtypes = fwd + [ctypes.POINTER(vp), ctypes.c_int]
         L.moe_experts_forward_timed.restype = ctypes.c_int
+        L.moe_experts_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_experts_forward_noalloc.restype = ctypes.c_int
         L.moe_align_workspace_bytes.argtypes = [i32, i32, i32]
         L.moe_align_workspace_bytes.restype = sz
         L.moe_align.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -154,6 +156,13 @@ def moe_experts_forward_timed(p: MoeProblem, x, topk_ids, topk_weights, w_gate, 
                                            _ptr(s_down), _ptr(out), _ptr(workspace),
                                            workspace.numel() * workspace.element_size(), _stream(stream), arr,
                                            len(events))
+
+
+def moe_experts_forward_noalloc(p: MoeProblem, x, topk_ids, topk_weights, w_gate, w_up, w_down, s_gate, s_up,
+                                s_down, out, stream=None) -> int:
+    return lib().moe_experts_forward_noalloc(ctypes.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights),
+                                             _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate), _ptr(s_up),
+                                             _ptr(s_down), _ptr(out), _stream(stream))
 
 
 def moe_align_workspace_bytes(T: int, k: int, E: int) -> int:

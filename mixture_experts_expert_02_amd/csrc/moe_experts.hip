@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe_experts.h"
 #include "align.hpp"
@@ -29,6 +30,31 @@ constexpr int kFusedMaxRows = 4096;
 constexpr int kFusedMaxExperts = 1024;
 constexpr size_t kAlign = 256;
 constexpr int kMaxSplitK = 4;
+
+// Workspace of moe_experts_forward_noalloc: one array per device, held from
+// the library's load until the process ends. Host code never uses its name
+// as an address: each device's copy is reached through the pointer that
+// hipGetSymbolAddress returns with that device current (scratch_on_device).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch address, looked up once per device (no allocation).
+int scratch_on_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 size_t up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -525,6 +551,20 @@ int moe_experts_forward_timed(const moe_problem* p, const void* x, const int32_t
                               void* const* stage_events, int n_events) {
   return forward_impl(p, x, topk_ids, topk_weights, w_gate, w_up, w_down, s_gate, s_up, s_down, out, workspace,
                       workspace_bytes, (hipStream_t)stream, stage_events, n_events);
+}
+
+int moe_experts_forward_noalloc(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                                const float* topk_weights, const void* w_gate, const void* w_up, const void* w_down,
+                                const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down, void* out,
+                                moe_stream_t stream) {
+  const int rc = check_problem(p, false);
+  if (rc) return rc;
+  if (p->T > 0 && make_plan(*p, false, kScratchBytes).total > kScratchBytes) return MOE_ENOSPC;
+  void* ws = nullptr;
+  const int r = scratch_on_device(&ws);
+  if (r) return r;
+  return forward_impl(p, x, topk_ids, topk_weights, w_gate, w_up, w_down, s_gate, s_up, s_down, out, ws,
+                      kScratchBytes, (hipStream_t)stream, nullptr, 0);
 }
 
 size_t moe_align_workspace_bytes(int32_t T, int32_t k, int32_t E) {

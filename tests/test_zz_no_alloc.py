@@ -1,0 +1,75 @@
+"""moe_experts_forward_noalloc (the library's own scratch as workspace)
+against moe_experts_forward on the same inputs: calls in a row, the second
+on a smaller problem than the first, each bitwise equal to the workspace
+entry point's output and within the tolerance of the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import TOL, rel_err, to_np, wl_act_kw
+from mixture_experts_expert_02_amd import binding as B
+from test_gpu_forward import ACT_PARAMS, make_problem
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda")
+
+
+def both(p, x, ids, w, W, S):
+    """(output of moe_experts_forward, output of moe_experts_forward_noalloc)."""
+    sg, su, sd = S if S is not None else (None, None, None)
+    ws = B.alloc_workspace(B.moe_experts_workspace_bytes(p), DEV)
+    ref = torch.empty(x.shape[0], x.shape[1], dtype=torch.bfloat16, device=DEV)
+    rc = B.moe_experts_forward(p, x, ids, w, *W, sg, su, sd, ref, ws)
+    assert rc == 0, B.strerror(rc)
+    got = torch.full_like(ref, float("nan"))
+    rc = B.moe_experts_forward_noalloc(p, x, ids, w, *W, sg, su, sd, got)
+    assert rc == 0, B.strerror(rc)
+    torch.cuda.synchronize()
+    return ref, got
+
+
+def test_noalloc_matches_workspace_entry_two_calls():
+    # call 1: the MXFP4 decode workload at full size
+    wl = synth.workload("mxfp4_decode")
+    print(f"[noalloc] call 1: {wl.name} T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.k}", flush=True)
+    ids, w = synth.make_routing(wl)
+    x = synth.make_x(wl, device=DEV)
+    (cg, sg), (cu, su), (cd, sd) = synth.make_mxfp4_weights(wl, device=DEV)
+    kw = wl_act_kw(wl)
+    p = B.problem(wl.T, wl.H, wl.I, wl.E, wl.k, "mxfp4", **kw)
+    ids_d, w_d = torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
+    ref, got = both(p, x, ids_d, w_d, (cg, cu, cd), (sg, su, sd))
+    assert torch.equal(ref, got)
+    want = oracle.experts_forward(to_np(x), ids, w, *[(c.cpu().numpy(), s.cpu().numpy()) for c, s in
+                                                     ((cg, sg), (cu, su), (cd, sd))], **kw)
+    assert rel_err(to_np(got), want) <= TOL
+    # call 2: a smaller MXFP4 problem (fewer tokens, smaller sizes) on the same scratch
+    T, H, I, E, k = 9, 256, 320, 6, 3
+    print(f"[noalloc] call 2: mxfp4 T={T} H={H} I={I} E={E} k={k}", flush=True)
+    x2, ids2, w2, W2, S2 = make_problem(43, T, H, I, E, k, "mxfp4")
+    p2 = B.problem(T, H, I, E, k, "mxfp4", "swiglu_oai", **ACT_PARAMS["swiglu_oai"])
+    ref2, got2 = both(p2, x2.to(DEV), torch.from_numpy(ids2).to(DEV), torch.from_numpy(w2).to(DEV),
+                      [t.to(DEV) for t in W2], [t.to(DEV) for t in S2])
+    assert torch.equal(ref2, got2)
+    want2 = oracle.experts_forward(to_np(x2), ids2, w2, *[(c.numpy(), s.numpy()) for c, s in zip(W2, S2)],
+                                   act="swiglu_oai", **ACT_PARAMS["swiglu_oai"])
+    assert rel_err(to_np(got2), want2) <= TOL
+    # call 3: bf16 weights on the LDS-tiled prefill GEMMs (K of the down projection split)
+    T, H, I, E, k = 300, 256, 384, 5, 2
+    print(f"[noalloc] call 3: bf16 T={T} H={H} I={I} E={E} k={k}", flush=True)
+    x3, ids3, w3, W3, _ = make_problem(41, T, H, I, E, k, "bf16")
+    p3 = B.problem(T, H, I, E, k, "bf16", "silu")
+    ref3, got3 = both(p3, x3.to(DEV), torch.from_numpy(ids3).to(DEV), torch.from_numpy(w3).to(DEV),
+                      [t.to(DEV) for t in W3], None)
+    assert torch.equal(ref3, got3)
+    want3 = oracle.experts_forward(to_np(x3), ids3, w3, *[to_np(t) for t in W3])
+    assert rel_err(to_np(got3), want3) <= TOL
+
+
+def test_noalloc_rejects_problems_beyond_the_scratch():
+    p = B.problem(4096, 4096, 14336, 8, 2)  # about 0.6 GB of workspace
+    x = torch.empty(1, dtype=torch.uint8, device=DEV)
+    rc = B.moe_experts_forward_noalloc(p, x, x, x, x, x, x, None, None, None, x)
+    assert rc == B.MOE_ENOSPC

@@ -108,6 +108,22 @@ typedef struct {
                               input-weighted top-1 routing). Costs one more read and
                               write of the routed rows. */
   int32_t a_fmt;           /* moe_afmt; 0 (bf16) when zero-initialised */
+  /* Per-expert parameters (device float32 arrays of E values, 4-byte aligned;
+   * NULL, the zero-initialised default, keeps the scalar above, or a scale
+   * of 1, for every expert). trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsBase
+   * constructor: the activation's alpha, beta and clamp limit are kept as
+   * per-expert tensors; flashinfer_moe_ep page, epilogue_from_quant_config:
+   * one weight global scale per expert becomes the fc1 alpha (multiplies the
+   * gate and up products of that expert's rows, before the activation) and
+   * the fc2 alpha (multiplies the down product). The library reads them on
+   * the device at every call and does not validate them there: check them
+   * once on the host with moe_check_expert_params. For the pre-grouped entry
+   * the index is the segment (E = segments). */
+  const float* alpha_e;
+  const float* beta_e;
+  const float* limit_e;
+  const float* fc1_alpha;
+  const float* fc2_alpha;
 } moe_problem;
 
 /* Byte offsets of the intermediates inside a forward workspace (for tests and
@@ -308,6 +324,20 @@ int moe_experts_forward_grouped_timed(const moe_problem* p, const void* x_nvs, c
  * outside [0, E) other than -1 in the last call (or 1 if its cu_seqlens were
  * malformed). Synchronous copy: call after the stream has finished. */
 int moe_device_error(const void* workspace, int32_t* n_bad);
+
+/*
+ * Host-side check of per-expert parameter arrays before they are uploaded
+ * (flashinfer_moe_ep page, epilogue_from_quant_config: the scales must be
+ * finite and positive, one per expert). Each pointer is a HOST array of p->E
+ * float32 values, or NULL (not checked). Rules, per expert, as for the
+ * scalars of moe_problem: fc1_alpha and fc2_alpha finite and > 0; for
+ * SwiGLU-OAI alpha and beta finite and limit > 0 (+inf allowed, NaN not);
+ * for SiTu alpha and beta finite and > 0. Returns MOE_OK, MOE_EINVAL (a
+ * non-finite value, a NaN limit, a bad problem) or MOE_ENOTSUP (a limit or a
+ * SiTu parameter <= 0, a scale <= 0). Reads host memory only.
+ */
+int moe_check_expert_params(const moe_problem* p, const float* alpha_e, const float* beta_e,
+                            const float* limit_e, const float* fc1_alpha, const float* fc2_alpha);
 
 /* Static description of a status code. */
 const char* moe_strerror(int status);

@@ -30,6 +30,7 @@ EXPORTED = (
     "moe_experts_forward_timed", "moe_align_workspace_bytes", "moe_align",
     "moe_experts_grouped_workspace_bytes", "moe_experts_forward_grouped", "moe_device_error",
     "moe_strerror", "moe_route", "moe_experts_forward_grouped_timed", "moe_experts_forward_noalloc",
+    "moe_check_expert_params",
 )
 MOE_ROUTE_RENORMALIZE, MOE_ROUTE_DEEPSEEK_V3 = 0, 1
 _ROUTE = {"renormalize": MOE_ROUTE_RENORMALIZE, "deepseek_v3": MOE_ROUTE_DEEPSEEK_V3}
@@ -39,7 +40,9 @@ class MoeProblem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("wfmt", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
-                ("limit", ctypes.c_float), ("weight_on_input", ctypes.c_int32), ("a_fmt", ctypes.c_int32)]
+                ("limit", ctypes.c_float), ("weight_on_input", ctypes.c_int32), ("a_fmt", ctypes.c_int32),
+                ("alpha_e", ctypes.c_void_p), ("beta_e", ctypes.c_void_p), ("limit_e", ctypes.c_void_p),
+                ("fc1_alpha", ctypes.c_void_p), ("fc2_alpha", ctypes.c_void_p)]
 
 
 class MoeRouteProblem(ctypes.Structure):
@@ -98,6 +101,9 @@ def lib() -> ctypes.CDLL:
         L.moe_device_error.restype = ctypes.c_int
         L.moe_route.argtypes = [ctypes.POINTER(MoeRouteProblem), vp, vp, vp, vp, vp]
         L.moe_route.restype = ctypes.c_int
+        fp = ctypes.POINTER(ctypes.c_float)
+        L.moe_check_expert_params.argtypes = [P, fp, fp, fp, fp, fp]
+        L.moe_check_expert_params.restype = ctypes.c_int
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -108,11 +114,37 @@ def strerror(status: int) -> str:
     return lib().moe_strerror(status).decode()
 
 
+EXPERT_PARAMS = ("alpha_e", "beta_e", "limit_e", "fc1_alpha", "fc2_alpha")
+
+
 def problem(T, H, I, E, k=1, wfmt="bf16", act="silu", alpha=1.0, beta=0.0, limit=math.inf,
-            weight_on_input=False, act_fmt="bf16") -> MoeProblem:
-    return MoeProblem(int(T), int(H), int(I), int(E), int(k), _WFMT[wfmt] if isinstance(wfmt, str) else int(wfmt),
-                      _ACT[act] if isinstance(act, str) else int(act), float(alpha), float(beta), float(limit),
-                      int(weight_on_input), _AFMT[act_fmt] if isinstance(act_fmt, str) else int(act_fmt))
+            weight_on_input=False, act_fmt="bf16", expert_params=None) -> MoeProblem:
+    """expert_params: optional dict from EXPERT_PARAMS names to device float32
+    tensors of E values (their pointers go into the problem)."""
+    p = MoeProblem(int(T), int(H), int(I), int(E), int(k), _WFMT[wfmt] if isinstance(wfmt, str) else int(wfmt),
+                   _ACT[act] if isinstance(act, str) else int(act), float(alpha), float(beta), float(limit),
+                   int(weight_on_input), _AFMT[act_fmt] if isinstance(act_fmt, str) else int(act_fmt))
+    for name, t in (expert_params or {}).items():
+        if name not in EXPERT_PARAMS:
+            raise KeyError(name)
+        setattr(p, name, None if t is None else t.data_ptr())
+    return p
+
+
+def moe_check_expert_params(p: MoeProblem, alpha_e=None, beta_e=None, limit_e=None, fc1_alpha=None,
+                            fc2_alpha=None) -> int:
+    """Host-side check; each argument None or a sequence / CPU tensor of p.E floats."""
+    keep = []
+
+    def arr(v):
+        if v is None:
+            return None
+        a = (ctypes.c_float * p.E)(*[float(x) for x in (v.tolist() if hasattr(v, "tolist") else v)])
+        keep.append(a)
+        return ctypes.cast(a, ctypes.POINTER(ctypes.c_float))
+
+    return lib().moe_check_expert_params(ctypes.byref(p), arr(alpha_e), arr(beta_e), arr(limit_e), arr(fc1_alpha),
+                                         arr(fc2_alpha))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -219,14 +251,14 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
 
 def experts_forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, scales=None, act="silu", alpha=1.0, beta=0.0,
                     limit=math.inf, out=None, workspace=None, weight_on_input=False,
-                    act_fmt="bf16") -> torch.Tensor:
+                    act_fmt="bf16", expert_params=None) -> torch.Tensor:
     """Token-major experts step on torch tensors; allocates out/workspace if not given."""
     T, H = x.shape
     k = topk_ids.shape[1]
     E = w_gate.shape[0]
     wfmt = "mxfp4" if w_gate.dtype == torch.uint8 else "bf16"
     I = w_gate.shape[1]
-    p = problem(T, H, I, E, k, wfmt, act, alpha, beta, limit, weight_on_input, act_fmt)
+    p = problem(T, H, I, E, k, wfmt, act, alpha, beta, limit, weight_on_input, act_fmt, expert_params)
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
     if workspace is None:
@@ -239,12 +271,12 @@ def experts_forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, scales=None
 
 def experts_forward_grouped(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, scales=None, act="silu", alpha=1.0,
                             beta=0.0, limit=math.inf, out=None, workspace=None, weight_on_input=False,
-                            act_fmt="bf16") -> torch.Tensor:
+                            act_fmt="bf16", expert_params=None) -> torch.Tensor:
     NvS, H = x_nvs.shape
     G = w_gate.shape[0]
     I = w_gate.shape[1]
     wfmt = "mxfp4" if w_gate.dtype == torch.uint8 else "bf16"
-    p = problem(NvS, H, I, G, 1, wfmt, act, alpha, beta, limit, weight_on_input, act_fmt)
+    p = problem(NvS, H, I, G, 1, wfmt, act, alpha, beta, limit, weight_on_input, act_fmt, expert_params)
     if out is None:
         out = torch.empty(NvS, H, dtype=torch.bfloat16, device=x_nvs.device)
     if workspace is None:

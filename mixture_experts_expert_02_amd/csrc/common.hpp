@@ -57,6 +57,30 @@ __device__ __forceinline__ float gated_act(const ActParams& a, float g, float u)
   return g * sigmoidf_fast(a.alpha * g) * (u + a.beta);
 }
 
+// Per-expert parameters: device float32 arrays of one value per expert
+// (segment), or nullptr where the problem's scalar (or 1 for the scales)
+// holds for every expert. trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsBase
+// constructor: the activation's alpha, beta and clamp limit are per-expert
+// tensors; flashinfer_moe_ep page, epilogue_from_quant_config: one fc1 and one
+// fc2 alpha per expert, scaling the gate/up products and the down product.
+struct ExpertParams {
+  const float* alpha;
+  const float* beta;
+  const float* limit;
+  const float* fc1;
+  const float* fc2;
+};
+
+__device__ __forceinline__ ActParams act_for(const ActParams& a, const ExpertParams& e, int seg) {
+  ActParams r = a;
+  if (e.alpha) r.alpha = e.alpha[seg];
+  if (e.beta) r.beta = e.beta[seg];
+  if (e.limit) r.limit = e.limit[seg];
+  return r;
+}
+
+__device__ __forceinline__ float scale_for(const float* s, int seg) { return s ? s[seg] : 1.f; }
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const uint32_t lane = __lane_id();
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));

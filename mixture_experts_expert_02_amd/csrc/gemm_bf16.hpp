@@ -56,12 +56,14 @@ struct Params {
   int32_t n_tiles;         // column tiles
   int32_t gn;              // column tiles per tile group
   int32_t xcd_remap;       // 1: renumber workgroups so consecutive tiles share an XCD
+  int32_t persistent;      // 1: one workgroup per compute unit, looping over lockstep rounds of tiles
   int32_t s_cap;           // GEMM2: at most this many K ranges per tile (1 = no split)
   int32_t ncu;             // compute units of the device (one block each)
   int64_t c_split;         // elements between the partial outputs of consecutive K ranges
   uint16_t* C;             // [rows, N] bf16 output, sorted row order (GEMM2 split: [S, rows, N])
   const float* row_w;      // GEMM1: route weight per sorted row, or nullptr (weight already on the input)
   ActParams act;
+  ExpertParams ep;         // per-expert activation parameters and fc1 / fc2 scales
 };
 
 // A stage holds 256 rows x 64 K (128 bytes = eight 16-byte chunks per row)
@@ -101,45 +103,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt lgkmcnt(0)"                                                          \
                : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]))
 
-template <bool GATED>
-__global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
-  // NS stages of [A 32 KB | B 32 KB]
-  __shared__ u32x4 smem[NS * 2 * STAGE_U4];
-  constexpr uint32_t STAGE_BYTES = 2 * STAGE_U4 * 16;
-  constexpr uint32_t B_HALF = STAGE_U4 * 16;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA targets go in M0
-
-  // block -> work item -> (row tile, column tile[, K range]). Only the
-  // device knows the number of row tiles, so the grid covers an upper bound
-  // and the items are numbered compactly over the live ones: blocks past the
-  // last item exit, and they are the last blocks dispatched (blocks that exit
-  // at once, interleaved with live ones, have left whole shader engines idle).
-  // With xcd_remap (the hardware sends workgroup b to XCD b mod 8), each XCD
-  // takes a contiguous run of items, so tiles that share weight and row
-  // panels share an L2. Items: groups of gn column
-  // tiles, row tiles inside a group, column tile fastest. GEMM2 may split K
-  // into S ranges (split_k_count) when there are too few tiles to fill the
-  // last round; the K range is the fastest index, and each range writes its
-  // own partial output, summed by the combine.
-  const int mtl = p.status[2];
-  int nsplit = 1;
-  if (!GATED && p.s_cap > 1) nsplit = split_k_count(mtl * p.n_tiles, p.K / BK, p.ncu, p.s_cap);
-  const int n_live = mtl * p.n_tiles * nsplit;
-  int item = blockIdx.x;
-  if (p.xcd_remap) {
-    const int per = (n_live + 7) >> 3;
-    const int j = blockIdx.x >> 3;
-    if (j >= per) return;
-    item = (blockIdx.x & 7) * per + j;
-  }
-  if (item >= n_live) return;
-  const int split = item % nsplit;
+// Work item -> (row tile, column tile, K range). Items: groups of gn column
+// tiles, row tiles inside a group, column tile fastest, K range fastest of
+// all (GEMM2 may split K into nsplit ranges when there are too few tiles to
+// fill the last round; each range writes its own partial output, summed by
+// the combine).
+__device__ __forceinline__ void item_tile(const Params& p, int item, int mtl, int nsplit, int& mt, int& nt,
+                                          int& split) {
+  split = item % nsplit;
   const int tl = item / nsplit;
   const int full = p.n_tiles / p.gn;  // groups of exactly gn column tiles
-  int mt, nt;
   if (tl < full * mtl * p.gn) {
     const int span = mtl * p.gn;
     const int grp = tl / span;
@@ -152,6 +127,17 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
     mt = r_in / gl;
     nt = full * p.gn + (r_in - mt * gl);
   }
+}
+
+template <bool GATED>
+__device__ __forceinline__ void gemm_tile(const Params& p, int mt, int nt, int split, int nsplit,
+                                          lds_u32x4* smem) {
+  constexpr uint32_t STAGE_BYTES = 2 * STAGE_U4 * 16;
+  constexpr uint32_t B_HALF = STAGE_U4 * 16;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA targets go in M0
 
   const int seg = p.tile_seg[mt];
   const int row0 = p.tile_row0[mt];
@@ -210,7 +196,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   // the barriers.
   const bool active = rows > wm * 128;
   const int lr = lane & 31, lk = lane >> 5;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u32x4*)smem;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   uint32_t a_lane[KS], b_lane[KS];  // per k-substep byte address of fragment 0 inside a stage
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -344,10 +330,12 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   // 128 rows x 32 columns per pass, rows padded to 40 elements against bank
   // conflicts.
   constexpr int LDR = 40;
-  uint16_t* sc = (uint16_t*)&smem[wave * 1024];
+  lds_u16* sc = (lds_u16*)&smem[wave * 1024];
   const int wrows = min(128, rows - wm * 128);
   uint16_t* __restrict__ Cs = p.C + (size_t)split * p.c_split;
   const int wrow0 = row0 + wm * 128;
+  const ActParams ap = act_for(p.act, p.ep, seg);
+  const float es = scale_for(GATED ? p.ep.fc1 : p.ep.fc2, seg);  // fc1 on gate and up, fc2 on down
   const int cc = lane & 3;          // 16-byte chunk of a staged 64-byte row
   const int rr = lane >> 2;         // staged row within a group of 16
 #pragma unroll
@@ -367,8 +355,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
         for (int r3 = 0; r3 < 4; ++r3) {
           const int r = rq * 4 + r3;
           float v;
-          if (GATED) v = gated_act(p.act, acc[i][0][r], acc[i][1][r]) * w4[r3];
-          else v = acc[i][pass][r];
+          if (GATED) v = gated_act(ap, acc[i][0][r] * es, acc[i][1][r] * es) * w4[r3];
+          else v = acc[i][pass][r] * es;
           const __bf16 h = (__bf16)v;
           sc[(rbase + r3) * LDR + lr] = *(const uint16_t*)&h;
         }
@@ -380,10 +368,55 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
       for (int t = 0; t < 8; ++t) {
         const int row = t * 16 + rr;
         if (row < wrows)
-          *(u32x4*)(Cs + (size_t)(wrow0 + row) * N + col0) = *(const u32x4*)&sc[row * LDR + cc * 8];
+          *(u32x4*)(Cs + (size_t)(wrow0 + row) * N + col0) = *(const lds_u32x4*)&sc[row * LDR + cc * 8];
       }
     }
   }
+}
+
+// Only the device knows the number of row tiles, so the grid covers an upper
+// bound and the items are numbered compactly over the live ones.
+// One tile per workgroup: blocks past the last item exit, and they are the
+// last blocks dispatched (blocks that exit at once, interleaved with live
+// ones, have left whole shader engines idle). With xcd_remap (the hardware
+// sends workgroup b to XCD b mod 8), each XCD takes a contiguous run of
+// items, so tiles that share weight and row panels share an L2.
+// Persistent (grid = a multiple of 8 workgroups, one per compute unit): in
+// round r, the S = grid / 8 workgroups of XCD x take the S consecutive items
+// of block 8 r + x, so each XCD's compute units run one block of tiles at a
+// time, in step, and tiles of a block read the same panels of A and B at the
+// same K at about the same time.
+template <bool GATED>
+__global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
+  // NS stages of [A 32 KB | B 32 KB]
+  __shared__ u32x4 smem_arr[NS * 2 * STAGE_U4];
+  lds_u32x4* smem = (lds_u32x4*)smem_arr;
+  const int mtl = p.status[2];
+  int nsplit = 1;
+  if (!GATED && p.s_cap > 1) nsplit = split_k_count(mtl * p.n_tiles, p.K / BK, p.ncu, p.s_cap);
+  const int n_live = mtl * p.n_tiles * nsplit;
+  int mt, nt, split;
+  if (p.persistent) {
+    const int S = gridDim.x >> 3, x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    for (int r = 0;; ++r) {
+      const int item = (r * 8 + x) * S + j;
+      if (item >= n_live) break;
+      if (r) stage_barrier();  // every wave has read its staged results of the last tile
+      item_tile(p, item, mtl, nsplit, mt, nt, split);
+      gemm_tile<GATED>(p, mt, nt, split, nsplit, smem);
+    }
+    return;
+  }
+  int item = blockIdx.x;
+  if (p.xcd_remap) {
+    const int per = (n_live + 7) >> 3;
+    const int j = blockIdx.x >> 3;
+    if (j >= per) return;
+    item = (blockIdx.x & 7) * per + j;
+  }
+  if (item >= n_live) return;
+  item_tile(p, item, mtl, nsplit, mt, nt, split);
+  gemm_tile<GATED>(p, mt, nt, split, nsplit, smem);
 }
 
 }  // namespace big

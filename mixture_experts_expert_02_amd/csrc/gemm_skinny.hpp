@@ -100,9 +100,11 @@ struct Params {
   const int32_t* status;  // status[2] = number of row tiles
   int32_t mt_cap;
   int32_t n_tiles;        // ceil(N / block_cols)
-  uint16_t* C;
+  uint16_t* C;            // [rows, N] bf16 output (unused by GEMM1 with MXFP8 activations)
+  QRows Cq;               // GEMM1 with MXFP8 activations: the activation rows, quantized
   const float* row_w;     // route weight per sorted row, or nullptr (weight already on the input)
   ActParams act;
+  ExpertParams ep;        // per-expert activation parameters and fc1 / fc2 scales
 };
 
 __device__ __forceinline__ float sat448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
@@ -506,6 +508,46 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
 #undef MOE_SKINNY_STEP
 
   // 16x16 result layout: lane holds column (lane & 15), rows 4 (lane >> 4) + r.
+  const ActParams ap = act_for(p.act, p.ep, seg);
+  const float es = scale_for(GATED ? p.ep.fc1 : p.ep.fc2, seg);  // fc1 on gate and up, fc2 on down
+  if constexpr (GATED && A8) {
+    // MXFP8 activations: the down projection's input rows are quantized here,
+    // from the fp32 activation (times the route weight), with the same rule as
+    // quant_row<true>. A 32-value block of a row spans the 16 columns of two
+    // waves (w, w ^ 1): each wave reduces its magnitude over its 16 lanes,
+    // the pair exchanges the two halves through LDS. N is a multiple of 64
+    // here (the host requires I % 64 == 0), so every wave has columns.
+    __shared__ float half_amax[NW][BM];
+    float v[4], m[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = q * 4 + r;
+      v[r] = gated_act(ap, acc0[r] * es, acc1[r] * es) * (p.row_w && row < rows ? p.row_w[row0 + row] : 1.f);
+      m[r] = fabsf(v[r]);
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) m[r] = fmaxf(m[r], __shfl_xor(m[r], off));
+      if (l16 == 0) half_amax[wave][row] = m[r];
+    }
+    lds_barrier();
+    const int blk = (nt * block_cols(true) + wave * 16) / 32;
+    const int KBo = N / 32;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = q * 4 + r;
+      if (row >= rows) continue;
+      const float amax = fmaxf(m[r], half_amax[wave ^ 1][row]);
+      const int code = min(max((int)((__float_as_uint(amax) >> 23) & 0xffu) - 8, 0), 254);
+      const float inv = __uint_as_float((uint32_t)(254 - code) << 23);  // 2^(127 - code)
+      const int e = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(v[r] * inv), 0.f, 0, false);
+      p.Cq.hi[(size_t)(row0 + row) * N + c0] = (uint8_t)(e & 0xff);
+      uint8_t* sc_row = p.Cq.sc + (size_t)(row0 + row) * p.Cq.sc_stride;
+      if (l16 == 0 && (wave & 1) == 0) sc_row[blk] = (uint8_t)code;
+      // the row's scale bytes past its last block (up to the 16-byte padded
+      // stride) are 0, like the ones quant_row writes: GEMM2 reads them
+      if (nt == p.n_tiles - 1 && wave == 0 && KBo + l16 < p.Cq.sc_stride) sc_row[KBo + l16] = 0;
+    }
+    return;
+  }
   if (!wave_on) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -514,10 +556,10 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
     uint16_t* dst = p.C + (size_t)(row0 + row) * N;
     if (GATED) {
       if (c0 < N)
-        dst[c0] = f32_to_bf16_rne(gated_act(p.act, acc0[r], acc1[r]) * (p.row_w ? p.row_w[row0 + row] : 1.f));
+        dst[c0] = f32_to_bf16_rne(gated_act(ap, acc0[r] * es, acc1[r] * es) * (p.row_w ? p.row_w[row0 + row] : 1.f));
     } else {
-      if (c0 < N) dst[c0] = f32_to_bf16_rne(acc0[r]);
-      if (c1 < N) dst[c1] = f32_to_bf16_rne(acc1[r]);
+      if (c0 < N) dst[c0] = f32_to_bf16_rne(acc0[r] * es);
+      if (c1 < N) dst[c1] = f32_to_bf16_rne(acc1[r] * es);
     }
   }
 }

@@ -103,6 +103,9 @@ int check_problem(const moe_problem* p, bool grouped) {
   if (p->weight_on_input != 0 && p->weight_on_input != 1) return MOE_EINVAL;
   if (p->a_fmt != MOE_A_BF16 && p->a_fmt != MOE_A_MXFP8) return MOE_EINVAL;
   if (p->a_fmt == MOE_A_MXFP8 && p->wfmt != MOE_W_MXFP4) return MOE_ENOTSUP;  // block-scaled MFMA path only
+  const void* ep[] = {p->alpha_e, p->beta_e, p->limit_e, p->fc1_alpha, p->fc2_alpha};
+  for (const void* q : ep)
+    if (((uintptr_t)q & 3u) != 0) return MOE_EINVAL;
   if (p->H % 64 || p->I % 64) return MOE_ENOTSUP;
   if (p->wfmt == MOE_W_MXFP4 && (p->H > moe::skinny::kMaxMxfp4K || p->I > moe::skinny::kMaxMxfp4K))
     return MOE_ENOTSUP;
@@ -226,6 +229,10 @@ moe::ActParams act_params(const moe_problem& p) {
   return a;
 }
 
+moe::ExpertParams expert_params(const moe_problem& p) {
+  return moe::ExpertParams{p.alpha_e, p.beta_e, p.limit_e, p.fc1_alpha, p.fc2_alpha};
+}
+
 // Compute units of the current device, cached per device.
 int device_cus(int* n) {
   static int cache[64] = {};
@@ -280,6 +287,17 @@ int group_cols_override() {
   return v;
 }
 
+// Tuning override for the prefill GEMM's schedule: MOE_EXPERTS_PERSISTENT=1
+// (one workgroup per compute unit, lockstep rounds) or 0 (one workgroup per
+// tile); read once; unset = built-in choice.
+int persistent_override() {
+  static const int v = [] {
+    const char* e = std::getenv("MOE_EXPERTS_PERSISTENT");
+    return e ? (std::atoi(e) != 0 ? 1 : 0) : -1;
+  }();
+  return v;
+}
+
 bool g_attr_done = false;
 int set_attrs() {
   if (g_attr_done) return MOE_OK;
@@ -326,6 +344,7 @@ struct GemmIO {
   int s_cap;         // GEMM2: K ranges with room in C (1 = C is [rows, N])
   long long c_split; // elements between partial outputs
   moe::skinny::QRows Aq;  // A split for the block-scaled MFMA (MXFP4 weights)
+  moe::skinny::QRows Cq;  // GEMM1 with MXFP8 activations: C quantized instead of written as bf16
 };
 
 template <bool GATED>
@@ -353,8 +372,10 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     q.mt_cap = pl.mt_cap;
     q.n_tiles = ceil_div(io.N, moe::skinny::block_cols(GATED));
     q.C = (uint16_t*)io.C;
+    q.Cq = io.Cq;
     q.row_w = io.row_w;
     q.act = act_params(p);
+    q.ep = expert_params(p);
     const dim3 grid((unsigned)pl.mt_cap * q.n_tiles);
     const dim3 block(moe::skinny::NT);
     using moe::skinny::k_gemm;
@@ -395,6 +416,7 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     q.C = (uint16_t*)io.C;
     q.row_w = io.row_w;
     q.act = act_params(p);
+    q.ep = expert_params(p);
     q.gn = std::min(q.n_tiles, group_cols_override() ? group_cols_override() : 2);
     q.xcd_remap = 1;
     q.s_cap = GATED ? 1 : io.s_cap;
@@ -404,6 +426,9 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     long long nblk = (long long)pl.mt_cap * q.n_tiles * q.s_cap;
     nblk = (nblk + 7) / 8 * 8;
     if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
+    const int po = persistent_override();
+    q.persistent = po < 0 ? 0 : po;
+    if (q.persistent) nblk = std::max(8, q.ncu / 8 * 8);
     hipLaunchKernelGGL((moe::big::k_gemm<GATED>), dim3((unsigned)nblk), dim3(moe::big::NT), 0, s, q);
   }
   return launch_status();
@@ -469,7 +494,9 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
     return rc;
   }
 
-  GemmIO g1{x, o.perm, p->k, wg, wu, sg, su, p->I, p->H, at<void>(ws, pl.act), o.w_sorted, 1, 0, {}};
+  GemmIO g1{x, o.perm, p->k, wg, wu, sg, su, p->I, p->H, at<void>(ws, pl.act), o.w_sorted, 1, 0, {}, {}};
+  // MXFP8 activations: GEMM1's epilogue quantizes the activation rows for GEMM2 itself
+  if (mx8) g1.Cq = quant_rows_at(ws, pl.aq, pl.M, p->I);
   if (p->weight_on_input) {  // rows x * w in sorted order; no weight in GEMM1's epilogue
     g1.A = at<void>(ws, pl.xs);
     g1.a_perm = nullptr;
@@ -494,10 +521,10 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
 
   const long long y_split = pl.M * p->H;
   GemmIO g2{at<void>(ws, pl.act), nullptr, 1, wd, nullptr, sd, nullptr, p->H, p->I, at<void>(ws, pl.y), nullptr,
-            pl.s_cap, y_split, {}};
+            pl.s_cap, y_split, {}, {}};
   if (mx) g2.Aq = quant_rows_at(ws, pl.aq, pl.M, p->I);
   mark(2);
-  if (mx) launch_quant(mx8, g2.A, pl.M, p->I, g2.Aq, s);
+  if (mx && !mx8) launch_quant(false, g2.A, pl.M, p->I, g2.Aq, s);
   if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
 
   mark(3);
@@ -649,7 +676,8 @@ int grouped_impl(const moe_problem* p, const void* x_nvs, const int32_t* cu_seql
   if ((rc = launch_status())) return rc;
   const bool mx = p->wfmt == MOE_W_MXFP4;
   const bool mx8 = p->a_fmt == MOE_A_MXFP8;
-  GemmIO g1{x_nvs, nullptr, 1, w_gate, w_up, s_gate, s_up, p->I, p->H, at<void>(ws, pl.act), route_w, 1, 0, {}};
+  GemmIO g1{x_nvs, nullptr, 1, w_gate, w_up, s_gate, s_up, p->I, p->H, at<void>(ws, pl.act), route_w, 1, 0, {}, {}};
+  if (mx8) g1.Cq = quant_rows_at(ws, pl.aq, pl.M, p->I);
   if (p->weight_on_input) {
     g1.A = at<void>(ws, pl.xs);
     g1.row_w = nullptr;
@@ -663,11 +691,12 @@ int grouped_impl(const moe_problem* p, const void* x_nvs, const int32_t* cu_seql
     launch_quant(mx8, g1.A, pl.M, p->H, g1.Aq, s);
   }
   if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
-  GemmIO g2{at<void>(ws, pl.act), nullptr, 1, w_down, nullptr, s_down, nullptr, p->H, p->I, out_nvs, nullptr, 1, 0, {}};
+  GemmIO g2{at<void>(ws, pl.act), nullptr, 1, w_down, nullptr, s_down, nullptr, p->H, p->I, out_nvs, nullptr, 1, 0, {},
+            {}};
   mark(2);
   if (mx) {
     g2.Aq = quant_rows_at(ws, pl.aq, pl.M, p->I);
-    launch_quant(mx8, g2.A, pl.M, p->I, g2.Aq, s);
+    if (!mx8) launch_quant(false, g2.A, pl.M, p->I, g2.Aq, s);
   }
   if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
   mark(3);
@@ -745,6 +774,27 @@ int moe_device_error(const void* workspace, int32_t* n_bad) {
   // status word sits at offset 0 of every workspace layout
   const hipError_t e = hipMemcpy(n_bad, workspace, sizeof(int32_t), hipMemcpyDeviceToHost);
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_check_expert_params(const moe_problem* p, const float* alpha_e, const float* beta_e,
+                            const float* limit_e, const float* fc1_alpha, const float* fc2_alpha) {
+  if (!p || p->E <= 0) return MOE_EINVAL;
+  for (int e = 0; e < p->E; ++e) {
+    for (const float* s : {fc1_alpha, fc2_alpha}) {
+      if (!s) continue;
+      if (!std::isfinite(s[e])) return MOE_EINVAL;
+      if (!(s[e] > 0.f)) return MOE_ENOTSUP;
+    }
+    if (p->act == MOE_ACT_SWIGLU_OAI) {
+      if ((alpha_e && !std::isfinite(alpha_e[e])) || (beta_e && !std::isfinite(beta_e[e]))) return MOE_EINVAL;
+      if (limit_e && std::isnan(limit_e[e])) return MOE_EINVAL;
+      if (limit_e && !(limit_e[e] > 0.f)) return MOE_ENOTSUP;
+    } else if (p->act == MOE_ACT_SITU) {
+      if ((alpha_e && !std::isfinite(alpha_e[e])) || (beta_e && !std::isfinite(beta_e[e]))) return MOE_EINVAL;
+      if ((alpha_e && !(alpha_e[e] > 0.f)) || (beta_e && !(beta_e[e] > 0.f))) return MOE_ENOTSUP;
+    }
+  }
+  return MOE_OK;
 }
 
 const char* moe_strerror(int status) {

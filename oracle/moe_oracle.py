@@ -39,10 +39,14 @@ Readings where the pages are silent:
     code clamped to [0, 254] (code 0 when amax = 0); each value becomes
     rne_e4m3(v / X), saturated at +-448, times X. Both GEMM inputs are
     quantized this way: the token rows before the gate and up GEMMs, the
-    activation rows (after the route weight) before the down GEMM. The
-    quantizer's input is a bf16 activation tensor (the model's activations
-    are bf16; the scheme quantizes them dynamically), so a row computed here
-    in float64 is rounded to bf16 (to nearest even) first.
+    activation rows (after the route weight) before the down GEMM. The token
+    rows are the bf16 tensor handed to the experts step, quantized as they
+    are (with the route weight on the input, the weighted rows are first
+    rounded to bf16, the form in which the prepare step hands activations
+    over: moonep_experts page, MoonEPExperts.apply). The activation rows are
+    quantized from their exact value: the flashinfer_moe_ep page
+    (epilogue_from_quant_config) quantizes activations dynamically inside the
+    kernel, so no bf16 tensor of them exists in between.
 
 Parity unpinned (the pages give a name and parameters but no formula, so the
 pins check this code against the reading, not against the pages): the
@@ -248,12 +252,15 @@ def bf16_round(v) -> np.ndarray:
     return np.sign(v) * np.round(a / q) * q
 
 
-def _act_in(rows: np.ndarray, act_fmt: str) -> np.ndarray:
-    """A GEMM's input rows as the GEMM sees them."""
+def _act_in(rows: np.ndarray, act_fmt: str, bf16_first: bool) -> np.ndarray:
+    """A GEMM's input rows as the GEMM sees them. With MXFP8 activations the
+    rows are quantized; bf16_first: they are a bf16 tensor (the token rows, or
+    the weighted token rows rounded to bf16), else their exact value (the
+    activation rows, quantized inside the experts step)."""
     if act_fmt == "bf16":
         return rows
     if act_fmt == "mxfp8":
-        return mxfp8_quantize(bf16_round(rows))[0]
+        return mxfp8_quantize(bf16_round(rows) if bf16_first else rows)[0]
     raise ValueError(f"unknown activation format {act_fmt!r}")
 
 
@@ -269,13 +276,39 @@ def expert_matrix(w: Weight, e: int) -> np.ndarray:
 # The experts computation in grouped form.
 # moonep_experts page, module docstring + MoonEPExperts.apply.
 # ----------------------------------------------------------------------------
+def _per_expert(v, e):
+    """Parameter v for expert (segment) e: v itself when it is a scalar, else
+    its entry e (one value per expert)."""
+    return v if np.ndim(v) == 0 else float(np.asarray(v, dtype=np.float64)[e])
+
+
+def _per_row(v, cu_seqlens: Sequence[int], n_rows: int):
+    """A per-expert parameter spread over the rows of a grouped problem: the
+    scalar itself, or a float64 column [n_rows, 1] holding each row's segment's
+    value (rows past the last end take the last segment's; they are zeroed)."""
+    if v is None or np.ndim(v) == 0:
+        return v
+    seg = np.searchsorted(np.asarray(cu_seqlens), np.arange(n_rows), side="right")
+    seg = np.minimum(seg, len(cu_seqlens) - 1)
+    return np.asarray(v, dtype=np.float64)[seg][:, None]
+
+
 def experts_grouped(x_rows: np.ndarray, cu_seqlens: Sequence[int], route_w: np.ndarray,
                     w_gate: Weight, w_up: Weight, w_down: Weight,
                     act: str = "silu", alpha=1.0, beta=0.0, limit=math.inf,
-                    weight_on_input: bool = False, act_fmt: str = "bf16") -> np.ndarray:
+                    weight_on_input: bool = False, act_fmt: str = "bf16",
+                    fc1_alpha=None, fc2_alpha=None) -> np.ndarray:
     """Rows already contiguous per weight row: gate and up grouped GEMMs, the
     activation times the per-row route weight, the down grouped GEMM. Rows past
     the last end offset come out zero.
+
+    alpha, beta, limit: scalars, or one value per segment (the
+    trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsBase constructor, keeps the
+    activation's alpha, beta and clamp limit as per-expert tensors).
+    fc1_alpha, fc2_alpha: None, or one scale per segment that multiplies the
+    gate and up products (fc1) and the down product (fc2) of that segment's
+    rows (the flashinfer_moe_ep page, epilogue_from_quant_config: one weight
+    global scale per expert becomes the fc1 / fc2 epilogue alpha).
 
     weight_on_input: the route weight multiplies the input row before the gate
     and up GEMMs instead of the activation (moonep_experts page,
@@ -290,16 +323,22 @@ def experts_grouped(x_rows: np.ndarray, cu_seqlens: Sequence[int], route_w: np.n
     rw = np.asarray(route_w, dtype=np.float64)[:, None]
     if weight_on_input:
         x_rows = x_rows * rw
-    x_rows = _act_in(x_rows, act_fmt)
+    x_rows = _act_in(x_rows, act_fmt, bf16_first=True)
     gate = grouped_mm(x_rows, lambda g: expert_matrix(w_gate, g), cu_seqlens)
     if gate is None:                                    # every segment empty
         return np.zeros((NvS, H), dtype=np.float64)
     up = grouped_mm(x_rows, lambda g: expert_matrix(w_up, g), cu_seqlens)
-    a = activation(act, gate, up, alpha, beta, limit)
+    if fc1_alpha is not None:
+        s1 = _per_row(fc1_alpha, cu_seqlens, NvS)
+        gate, up = gate * s1, up * s1
+    a = activation(act, gate, up, _per_row(alpha, cu_seqlens, NvS), _per_row(beta, cu_seqlens, NvS),
+                   _per_row(limit, cu_seqlens, NvS))
     if not weight_on_input:
         a = a * rw
-    a = _act_in(a, act_fmt)
+    a = _act_in(a, act_fmt, bf16_first=False)
     out = grouped_mm(a, lambda g: expert_matrix(w_down, g), cu_seqlens)
+    if fc2_alpha is not None:
+        out = out * _per_row(fc2_alpha, cu_seqlens, NvS)
     end = int(cu_seqlens[-1]) if len(cu_seqlens) else 0
     out[end:] = 0.0
     return out
@@ -308,7 +347,8 @@ def experts_grouped(x_rows: np.ndarray, cu_seqlens: Sequence[int], route_w: np.n
 def experts_forward(x: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
                     w_gate: Weight, w_up: Weight, w_down: Weight,
                     act: str = "silu", alpha=1.0, beta=0.0, limit=math.inf,
-                    weight_on_input: bool = False, act_fmt: str = "bf16") -> np.ndarray:
+                    weight_on_input: bool = False, act_fmt: str = "bf16",
+                    fc1_alpha=None, fc2_alpha=None) -> np.ndarray:
     """Token-major MoE experts layer: group the routed slots by expert, run
     the grouped computation, then combine each token's k slot results in
     ascending j (flashinfer_moe_ep page: route, compute, combine)."""
@@ -321,7 +361,7 @@ def experts_forward(x: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarra
     x_rows = x[perm // k]
     rw = np.asarray(topk_weights, dtype=np.float64).reshape(-1)[perm]
     y = experts_grouped(x_rows, al["cu_seqlens"], rw, w_gate, w_up, w_down, act, alpha, beta, limit,
-                        weight_on_input, act_fmt)
+                        weight_on_input, act_fmt, fc1_alpha, fc2_alpha)
     out = np.zeros((T, x.shape[1]), dtype=np.float64)
     for t in range(T):
         acc = np.zeros(x.shape[1], dtype=np.float64)
@@ -335,7 +375,7 @@ def experts_forward(x: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarra
 
 def experts_forward_literal(x, topk_ids, topk_weights, w_gate, w_up, w_down,
                             act="silu", alpha=1.0, beta=0.0, limit=math.inf,
-                            weight_on_input=False, act_fmt="bf16") -> np.ndarray:
+                            weight_on_input=False, act_fmt="bf16", fc1_alpha=None, fc2_alpha=None) -> np.ndarray:
     """The per-token definition: for each token and each of its k slots, run
     the selected expert's MLP on the token, scale by the route weight, and sum
     over the slots in ascending j. Masked (-1) and out-of-range ids add
@@ -353,26 +393,31 @@ def experts_forward_literal(x, topk_ids, topk_weights, w_gate, w_up, w_down,
             if e < 0 or e >= E:
                 continue
             xin = x[t] * wts[t, j] if weight_on_input else x[t]
-            xin = _act_in(xin, act_fmt)
+            xin = _act_in(xin, act_fmt, bf16_first=True)
             g = expert_matrix(w_gate, e) @ xin
             u = expert_matrix(w_up, e) @ xin
-            a = activation(act, g, u, alpha, beta, limit)
+            if fc1_alpha is not None:
+                g, u = g * _per_expert(fc1_alpha, e), u * _per_expert(fc1_alpha, e)
+            a = activation(act, g, u, _per_expert(alpha, e), _per_expert(beta, e), _per_expert(limit, e))
             if not weight_on_input:
                 a = a * wts[t, j]
-            a = _act_in(a, act_fmt)
-            acc = acc + expert_matrix(w_down, e) @ a
+            a = _act_in(a, act_fmt, bf16_first=False)
+            yd = expert_matrix(w_down, e) @ a
+            if fc2_alpha is not None:
+                yd = yd * _per_expert(fc2_alpha, e)
+            acc = acc + yd
         out[t] = acc
     return out
 
 
 def pregrouped_forward(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down,
                        act="silu", alpha=1.0, beta=0.0, limit=math.inf, weight_on_input=False,
-                       act_fmt="bf16") -> np.ndarray:
+                       act_fmt="bf16", fc1_alpha=None, fc2_alpha=None) -> np.ndarray:
     """The pre-grouped entry: rows given in segment order with end offsets and
     per-row route weights (moonep_experts page, MoonEPExperts.apply). Same as
     `experts_grouped`; named for the entry point it checks."""
     return experts_grouped(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, act, alpha, beta, limit,
-                           weight_on_input, act_fmt)
+                           weight_on_input, act_fmt, fc1_alpha, fc2_alpha)
 
 
 def _num_experts(w: Weight) -> int:

@@ -228,3 +228,37 @@ def test_mxfp8_activations_need_mxfp4_weights():
     assert B.moe_experts_workspace_bytes(B.problem(32, 256, 256, 8, 2, wfmt="mxfp4", act_fmt=7)) == 0
     lay = B.moe_experts_workspace_layout(ok)
     assert lay.xq > 0 and lay.aq > lay.xq and lay.xq_rows == 32
+
+
+# ------------------------------------------------------------------ per-expert parameters
+def test_check_expert_params_host_rules():
+    E = 4
+    ok = [1.0, 0.5, 2.0, 3.0]
+    silu = B.problem(8, 128, 256, E, 2)
+    assert B.moe_check_expert_params(silu, fc1_alpha=ok, fc2_alpha=ok) == B.MOE_OK
+    for bad, code in (([1.0, math.nan, 1.0, 1.0], B.MOE_EINVAL), ([1.0, math.inf, 1.0, 1.0], B.MOE_EINVAL),
+                      ([1.0, 0.0, 1.0, 1.0], B.MOE_ENOTSUP), ([1.0, -2.0, 1.0, 1.0], B.MOE_ENOTSUP)):
+        assert B.moe_check_expert_params(silu, fc1_alpha=bad) == code
+        assert B.moe_check_expert_params(silu, fc2_alpha=bad) == code
+    oai = B.problem(8, 128, 256, E, 2, act="swiglu_oai", alpha=1.702, beta=1.0, limit=7.0)
+    assert B.moe_check_expert_params(oai, alpha_e=[1.7, -1.0, 0.0, 2.0], beta_e=[1.0, 0.0, -1.0, 1.0],
+                                     limit_e=[7.0, math.inf, 1.0, 3.0]) == B.MOE_OK
+    assert B.moe_check_expert_params(oai, limit_e=[7.0, math.nan, 1.0, 3.0]) == B.MOE_EINVAL
+    assert B.moe_check_expert_params(oai, limit_e=[7.0, 0.0, 1.0, 3.0]) == B.MOE_ENOTSUP
+    assert B.moe_check_expert_params(oai, alpha_e=[7.0, math.inf, 1.0, 3.0]) == B.MOE_EINVAL
+    situ = B.problem(8, 128, 256, E, 2, act="situ", alpha=1.5, beta=0.8)
+    assert B.moe_check_expert_params(situ, alpha_e=ok, beta_e=ok) == B.MOE_OK
+    assert B.moe_check_expert_params(situ, alpha_e=[1.0, 1.0, 0.0, 1.0]) == B.MOE_ENOTSUP
+    assert B.moe_check_expert_params(situ, beta_e=[1.0, 1.0, math.nan, 1.0]) == B.MOE_EINVAL
+    # a problem the scalar checks reject is rejected here too
+    assert B.moe_check_expert_params(B.problem(8, 128, 256, 0, 1)) == B.MOE_EINVAL
+
+
+def test_misaligned_expert_param_pointer_rejected():
+    for name in B.EXPERT_PARAMS:
+        p = B.problem(64, 128, 256, 8, 2)
+        setattr(p, name, (1 << 20) + 2)          # not 4-byte aligned; never dereferenced
+        assert B.moe_experts_workspace_bytes(p) == 0
+        fake = ctypes.c_void_p(1 << 20)
+        assert B.lib().moe_experts_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None, None,
+                                           fake, fake, 1 << 40, None) == B.MOE_EINVAL

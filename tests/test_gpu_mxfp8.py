@@ -1,8 +1,9 @@
 """MXFP8 activations with MXFP4 weights on the GPU (one e4m3 part per value
 into the block-scaled MFMA) against the oracle's MXFP8 mode: the quantized
-GEMM inputs bit for bit (token rows and activation rows, read from the
-workspace), the output within the tolerance, and the decode workload at full
-size on sampled tokens."""
+token rows bit for bit, the activation rows (quantized in GEMM1's epilogue
+from fp32) against the oracle's exact activation, the output within the
+tolerance (the margin printed per case), and the decode workload at full
+size."""
 import math
 import zlib
 
@@ -71,8 +72,59 @@ def test_mxfp8_split_rows_bit_exact(shape):
     check_split(ws, lay.xq, T, H, to_np(x), T)
     M = T * k
     n_valid = int(ws[lay.status + 4: lay.status + 8].view(torch.int32).item())
-    act = ws[lay.act: lay.act + M * I * 2].view(torch.bfloat16).view(M, I)
-    check_split(ws, lay.aq, M, I, to_np(act), n_valid)
+    check_epilogue_quant(ws, lay.aq, M, I, oracle_activation(x, ids, w, W, S, act_kw), n_valid)
+
+
+def oracle_activation(x, ids, w, W, S, act_kw):
+    """The oracle's down-projection input before quantization, in sorted row
+    order: the activation of the MXFP8-quantized token rows times the route
+    weight (float64)."""
+    E, k = W[0].shape[0], ids.shape[1]
+    al = oracle.align(ids, E)
+    xr = oracle.mxfp8_quantize(to_np(x)[al["perm"] // k])[0]
+    Wn = [(c.numpy(), s.numpy()) for c, s in zip(W, S)]
+    g = oracle.grouped_mm(xr, lambda e: oracle.expert_matrix(Wn[0], e), al["cu_seqlens"])
+    u = oracle.grouped_mm(xr, lambda e: oracle.expert_matrix(Wn[1], e), al["cu_seqlens"])
+    kw = {kk: v for kk, v in act_kw.items() if kk in ("alpha", "beta", "limit")}
+    a = oracle.activation(act_kw["act"], g, u, **kw)
+    return a * w.reshape(-1)[al["perm"]][:, None]
+
+
+def e4m3_spacing(v):
+    a = np.abs(v)
+    _, ex = np.frexp(a)
+    return np.ldexp(1.0, (np.maximum(ex - 1, -6) - 3).astype(np.int32))
+
+
+def check_epilogue_quant(ws, off, R, K, a64, nrows):
+    """GEMM1's epilogue quantizes the activation rows from their fp32 value;
+    the oracle from the float64 value. Scale codes must agree (except where
+    a block's largest magnitude lies within fp32 noise of a power of two),
+    and every e4m3 element must be one of the two grid neighbours of the
+    exact scaled value, the oracle's own rounding except within fp32 noise of
+    a rounding midpoint."""
+    sc_stride = (K // 32 + 15) // 16 * 16
+    hi = ws[off: off + R * K].view(R, K)[:nrows]
+    sc = ws[off + 2 * R * K: off + 2 * R * K + R * sc_stride].view(R, sc_stride)[:nrows]
+    codes = sc[:, : K // 32].cpu().numpy().astype(np.int64)
+    assert np.all(sc[:, K // 32:].cpu().numpy() == 0), "scale padding bytes not zero"
+    _, elem, want = oracle.mxfp8_quantize(a64[:nrows])
+    amax = np.abs(a64[:nrows]).reshape(nrows, K // 32, 32).max(axis=-1)
+    frac = amax / np.ldexp(1.0, np.frexp(amax)[1] - 1)          # in [1, 2)
+    near_pow2 = (np.abs(frac - 1) < 1e-4) | (np.abs(frac - 2) < 1e-4)
+    bad_codes = (codes != want) & ~near_pow2
+    assert not bad_codes.any(), f"{int(bad_codes.sum())} scale codes differ"
+    got = e4m3_bytes_to_f64(hi).reshape(nrows, K // 32, 32)
+    X = np.ldexp(1.0, (codes - 127).astype(np.int32))[..., None]
+    v = np.clip(a64[:nrows].reshape(nrows, K // 32, 32) / X, -448, 448)
+    sp = e4m3_spacing(v)
+    assert np.all(np.abs(got - v) <= sp * (1 + 1e-9)), "an element is not a neighbour of its exact value"
+    same_code = (codes == want)[..., None] & np.ones((1, 1, 32), dtype=bool)
+    diff = (got != elem.reshape(nrows, K // 32, 32)) & same_code
+    mid = np.abs(np.abs(v - got) - sp / 2) <= 1e-2 * sp
+    assert np.all(mid[diff]), f"{int((diff & ~mid).sum())} elements rounded differently away from a midpoint"
+    print(f"[mxfp8] epilogue quantization: {int(diff.sum())} of {diff.size} elements on the other side of a "
+          f"midpoint, {int(((codes != want) & near_pow2).sum())} scale codes at a power-of-two boundary", flush=True)
 
 
 CASES = [

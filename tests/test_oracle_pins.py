@@ -590,19 +590,73 @@ def test_bf16_round_matches_torch_and_closed_forms():
     assert oracle.bf16_round(np.array([0.0, -2.0 ** 100])).tolist() == [0.0, -2.0 ** 100]
 
 
-def test_mxfp8_mode_quantizes_the_bf16_activation():
-    # bf16 values are unchanged by the bf16 rounding, so on bf16 input rows the
+def test_mxfp8_mode_rounds_token_rows_to_bf16_but_not_activation_rows():
+    # bf16 values are unchanged by the bf16 rounding, so on bf16 token rows the
     # mode's first quantization is exactly mxfp8_quantize
     rng = np.random.default_rng(9)
     rows = torch.from_numpy(rng.standard_normal((4, 64)).astype(np.float32)).to(torch.bfloat16).double().numpy()
-    assert np.array_equal(oracle.moe_oracle._act_in(rows, "mxfp8"), oracle.mxfp8_quantize(rows)[0])
+    assert np.array_equal(oracle.moe_oracle._act_in(rows, "mxfp8", bf16_first=True), oracle.mxfp8_quantize(rows)[0])
     # an off-grid value that bf16 rounding moves onto an e4m3 midpoint: in a
     # block of amax 1.5 (scale 2^-8) the e4m3 neighbours of 1 + 2^-4 are 1 and
     # 1 + 2^-3; 1 + 2^-4 + 2^-10 rounds to 1 + 2^-4 in bf16 (8 bits), then to 1
-    # (even) in e4m3, while unrounded it goes up to 1 + 2^-3
+    # (even) in e4m3, while unrounded it goes up to 1 + 2^-3. Token rows (a
+    # bf16 tensor, or the weighted rows rounded to bf16) take the first path;
+    # activation rows, quantized from their exact value inside the step, the
+    # second.
     blk = np.zeros((1, 32))
     blk[0, 0] = 1.5
     blk[0, 1] = 1 + 2.0 ** -4 + 2.0 ** -10
-    got = oracle.moe_oracle._act_in(blk, "mxfp8")
-    assert got[0, 1] == 1.0
+    assert oracle.moe_oracle._act_in(blk, "mxfp8", bf16_first=True)[0, 1] == 1.0
+    assert oracle.moe_oracle._act_in(blk, "mxfp8", bf16_first=False)[0, 1] == 1 + 2.0 ** -3
     assert oracle.mxfp8_quantize(blk)[0][0, 1] == 1 + 2.0 ** -3
+
+
+# ------------------------------------------------------------------ per-expert parameters
+def test_per_expert_params_equal_scalars_when_constant():
+    x, ids, w, wg, wu, wd = rand_problem(31, T=9, H=32, I=64, E=4, k=2, masked=0.1)
+    kw = dict(act="swiglu_oai", alpha=1.702, beta=1.0, limit=7.0)
+    a = oracle.experts_forward(x, ids, w, wg, wu, wd, **kw)
+    b = oracle.experts_forward(x, ids, w, wg, wu, wd, act="swiglu_oai", alpha=np.full(4, 1.702),
+                               beta=np.full(4, 1.0), limit=np.full(4, 7.0), fc1_alpha=np.ones(4), fc2_alpha=np.ones(4))
+    assert np.array_equal(a, b)
+
+
+def test_fc1_fc2_alphas_equal_prescaled_weights_in_a_dense_torch_mlp():
+    # top-1, weight 1: each token's output is its expert's MLP, so scaling the
+    # gate / up products by fc1[e] and the down product by fc2[e] must equal a
+    # dense torch MLP whose weights were multiplied by those scales
+    x, ids, w, wg, wu, wd = rand_problem(32, T=12, H=32, I=64, E=3, k=1)
+    w[:] = 1.0
+    fc1 = np.array([0.7, 1.9, 0.25])
+    fc2 = np.array([3.0, 0.5, 1.3])
+    got = oracle.experts_forward(x, ids, w, wg, wu, wd, fc1_alpha=fc1, fc2_alpha=fc2)
+    X = torch.from_numpy(x.astype(np.float64))
+    for t in range(12):
+        e = int(ids[t, 0])
+        g = X[t] @ torch.from_numpy(wg[e].astype(np.float64) * fc1[e]).T
+        u = X[t] @ torch.from_numpy(wu[e].astype(np.float64) * fc1[e]).T
+        ref = (torch.nn.functional.silu(g) * u) @ torch.from_numpy(wd[e].astype(np.float64) * fc2[e]).T
+        assert np.allclose(got[t], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_per_expert_activation_params_are_the_union_of_scalar_runs():
+    # distinct alpha / beta / limit per expert: every token of a top-1
+    # problem gets exactly what the scalar oracle gives with its expert's values
+    x, ids, w, wg, wu, wd = rand_problem(33, T=16, H=32, I=64, E=4, k=1)
+    x = x * 3.0                      # reach the clamp limits
+    al = np.array([1.702, 0.5, 2.5, 1.0])
+    be = np.array([1.0, 0.0, -0.5, 2.0])
+    li = np.array([7.0, 0.3, np.inf, 1.5])
+    got = oracle.experts_forward(x, ids, w, wg, wu, wd, act="swiglu_oai", alpha=al, beta=be, limit=li)
+    lit = oracle.experts_forward_literal(x, ids, w, wg, wu, wd, act="swiglu_oai", alpha=al, beta=be, limit=li)
+    assert np.max(np.abs(got - lit)) <= 1e-12 * np.max(np.abs(lit))
+    for e in range(4):
+        rows = np.where(ids[:, 0] == e)[0]
+        if len(rows) == 0:
+            continue
+        ref = oracle.experts_forward(x[rows], ids[rows], w[rows], wg, wu, wd, act="swiglu_oai", alpha=al[e],
+                                     beta=be[e], limit=li[e])
+        assert np.array_equal(got[rows], ref)
+    # the experts' values really differ in effect
+    same = oracle.experts_forward(x, ids, w, wg, wu, wd, act="swiglu_oai", alpha=1.702, beta=1.0, limit=7.0)
+    assert np.max(np.abs(got - same)) > 1e-3 * np.max(np.abs(same))

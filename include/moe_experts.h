@@ -63,7 +63,9 @@ typedef enum {
   MOE_EINVAL = -1,  /* null pointer, non-positive size, k > E, unknown enum, non-finite parameter */
   MOE_ENOTSUP = -2, /* valid but unsupported: H or I not a multiple of 64, E > 4096, limit <= 0, ... */
   MOE_ENOSPC = -3,  /* workspace smaller than the *_workspace_bytes() figure for this problem */
-  MOE_EHIP = -4     /* a HIP launch or query failed */
+  MOE_EHIP = -4,    /* a HIP launch or query failed */
+  MOE_ETIMEDOUT = -5 /* moe_device_error: a bounded wait inside the single-launch decode step
+                        gave up (its results are invalid) */
 } moe_status;
 
 /* Weight format. trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsBase._supports_quant_scheme
@@ -149,6 +151,16 @@ typedef struct {
   size_t xq_rows;    /* T when split in token order (small problems, weight on the
                         activation), else T*k in sorted row order */
   size_t aq;         /* activation rows, K = I, R = T*k, sorted row order */
+  size_t single_launch; /* 1 when the forward runs the decode step as one launch after the
+                           align: weight-streaming tiles, the one-workgroup align, route
+                           weight on the activation, H and I <= 4096, and the environment
+                           variable MOE_EXPERTS_FUSED_DECODE=1 at the call (off by default:
+                           measured slower than the separate launches). GEMM1, GEMM2 and the
+                           combine then share one persistent kernel (flashinfer_moe_ep page,
+                           module docstring: one launch) and moe_experts_forward_timed records
+                           events 2, 3 and 4 together after it; act is not written with MXFP4
+                           weights (GEMM1 writes the split rows in aq). The workspace holds
+                           its counters either way. */
 } moe_ws_layout;
 
 /* Workspace bytes a moe_experts_forward call on problem *p needs (0 if *p is
@@ -319,10 +331,13 @@ int moe_experts_forward_grouped_timed(const moe_problem* p, const void* x_nvs, c
                                       size_t workspace_bytes, moe_stream_t stream,
                                       void* const* stage_events, int n_events);
 
-/* Reads the device status word of a workspace used by moe_experts_forward,
+/* Reads the device status words of a workspace used by moe_experts_forward,
  * moe_experts_forward_grouped or moe_align: *n_bad = number of expert ids
  * outside [0, E) other than -1 in the last call (or 1 if its cu_seqlens were
- * malformed). Synchronous copy: call after the stream has finished. */
+ * malformed). Returns MOE_ETIMEDOUT if a wait of the single-launch decode
+ * step gave up in that call (none ever should: every wait is on work that
+ * running workgroups took earlier; the bound only guarantees the kernel
+ * ends). Synchronous copy: call after the stream has finished. */
 int moe_device_error(const void* workspace, int32_t* n_bad);
 
 /*

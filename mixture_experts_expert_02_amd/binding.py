@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_experts.so")
 
-MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_ENOSPC, MOE_EHIP, MOE_ETIMEDOUT = 0, -1, -2, -3, -4, -5
 MOE_W_BF16, MOE_W_MXFP4 = 0, 1
 MOE_ACT_SILU, MOE_ACT_SWIGLU_OAI, MOE_ACT_SITU = 0, 1, 2
 
@@ -54,7 +54,7 @@ class MoeRouteProblem(ctypes.Structure):
 class MoeWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("status", "counts", "cu_seqlens", "perm", "inv_perm", "w_sorted", "act", "y", "total",
-                 "xq", "xq_rows", "aq")]
+                 "xq", "xq_rows", "aq", "single_launch")]
 
 
 class MoeError(RuntimeError):

@@ -26,7 +26,9 @@ struct AlignOut {
   float* w_sorted;     // [M] or nullptr
   int32_t* tile_seg;   // [mt_cap] tile -> segment
   int32_t* tile_row0;  // [mt_cap] tile -> first sorted row
-  int32_t* status;     // [4]: bad ids, valid rows, tiles, unused
+  int32_t* status;     // [4]: bad ids, valid rows, tiles, wait-timeout flag
+  int32_t* sync;       // counters the single-launch decode step expects zero, or nullptr
+  int32_t n_sync;
 };
 
 __device__ __forceinline__ int slot_key(const int32_t* ids, int i, int end, int E, int& bad) {
@@ -154,6 +156,8 @@ __device__ __forceinline__ void align_fused_body(const int32_t* ids, const float
   int32_t* scratch = mts + E;     // [16]
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   for (int i = tid; i < 4 * E; i += 256) hist[i] = 0;
+  if (o.sync)
+    for (int i = tid; i < o.n_sync; i += 256) o.sync[i] = 0;
   __syncthreads();
   const int chunk = ((M + 3) / 4 + 63) / 64 * 64;
   const int begin = min(wid * chunk, M), end = min(begin + chunk, M);

@@ -250,21 +250,120 @@ __device__ __forceinline__ void lds_barrier() {
 
 extern __shared__ __attribute__((aligned(16))) uint8_t skinny_scales[];
 
+// ---------------------------------------------------------------------------
+// Single-launch decode step. GEMM1 tiles, GEMM2 tiles and combine rows are
+// items of one work queue, taken in that order by the workgroups of one
+// persistent launch. Data one workgroup hands to another (GEMM1's activation
+// rows for GEMM2, GEMM2's slot rows for the combine) goes out with
+// agent-coherent stores, which write through the XCD's own L2, and is read
+// with agent-coherent loads, which skip stale L2 copies; a workgroup counts
+// itself in only after its stores have completed. Every wait is on items
+// with lower queue positions, which were taken by running workgroups that
+// never wait on later items, so the waits always end; each is still bounded
+// and sets a status flag if it gives up.
+struct FusedSync {
+  int32_t* queue;     // work-queue position (zero before the launch)
+  int32_t* done1;     // [row tiles]: GEMM1 column tiles finished per row tile (zero before)
+  int32_t* done2;     // GEMM2 tiles finished (zero before)
+  int32_t* status;    // status[3] = 1 when a wait gave up
+  int32_t n_tiles1;   // GEMM1 column tiles per row tile
+  int32_t spin_limit;
+  int32_t batch;      // consecutive items taken from the queue at a time (>= 1)
+};
+
+__device__ __forceinline__ void st_coh32(void* p, uint32_t v) {
+  __hip_atomic_store((uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh8(uint8_t* p, uint32_t v) {
+  __hip_atomic_store(p, (uint8_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes at base + off with the agent-coherence cache policy (sc1, the one
+// the compiler gives agent-scope atomic loads), through a buffer resource over
+// base so the load stays one instruction.
+constexpr int kAuxSc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xffffffffu, 0x00020000);
+}
+__device__ __forceinline__ u32x4 ld_coh128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxSc1);
+}
+
+// Control flow around the barriers of the single launch stays uniform
+// across the lanes of every wave: wave 0 (a wave-uniform condition) does the
+// waiting and the counting on all 64 lanes, and every loaded value that
+// decides a branch is made uniform with readfirstlane. A branch on a lane
+// condition (thread 0 only) inside the work loop lets the compiler run the
+// other lanes of the wave around the loop, barriers included, without it.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+
+// Wave 0 waits until *c >= target (or the status flag is set, or the spin
+// limit is reached, which sets the flag); the workgroup then meets at an
+// LDS-only barrier, so weight loads issued before the wait stay in flight.
+__device__ __forceinline__ void wait_count(const int32_t* c, int target, const FusedSync& fs) {
+  if (wave_id() == 0) {
+    for (int spins = 0;; ++spins) {
+      const int cur = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(const_cast<int32_t*>(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (cur >= target) break;
+      const int flag = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(&fs.status[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (flag != 0) break;
+      if (spins >= fs.spin_limit) {
+        __hip_atomic_store(&fs.status[3], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  lds_barrier();
+}
+
+// After a tile's coherent stores: every thread waits for its stores to
+// complete, the workgroup meets, and wave 0 counts the tile in (lane 0 adds
+// 1, the other lanes 0).
+__device__ __forceinline__ void count_in(int32_t* c) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+  if (wave_id() == 0)
+    __hip_atomic_fetch_add(c, (threadIdx.x & 63) == 0 ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The bytes b of the 16 lanes of a lane group (16 consecutive columns of one
+// row), four at a time: lanes with l16 % 4 == 0 get columns l16 .. l16 + 3.
+__device__ __forceinline__ uint32_t gather4(uint32_t b) {
+  return (b & 0xffu) | ((uint32_t)__shfl_down((int)b, 1) & 0xffu) << 8 |
+         ((uint32_t)__shfl_down((int)b, 2) & 0xffu) << 16 | ((uint32_t)__shfl_down((int)b, 3) & 0xffu) << 24;
+}
+
+// LDS of one decode tile: two activation buffers, the per-wave weight
+// rearrangement region (MXFP4), the block maxima exchanged by wave pairs.
+template <int FMT>
+struct TileLds {
+  static constexpr int kWtStep = 16 * 64 + 16;
+  __attribute__((aligned(16))) uint8_t sbuf[2][Cfg<FMT>::BUF_BYTES];
+  __attribute__((aligned(16))) uint8_t wtr[FMT == W_MXFP4 ? NW : 1][FMT == W_MXFP4 ? 8 * kWtStep : 16];
+  float half_amax[NW][BM];
+};
+
+// One tile: row tile mt, column tile nt.
 // SPT: scale pieces per thread (MXFP4; 0 for bf16), scale_pieces_per_thread(K).
 // A8: MXFP8 activations (MXFP4 weights): the rows hold one e4m3 part, so each
 // step runs one block-scaled MFMA per stream and loads no lo bytes.
-template <int FMT, bool GATED, int SPT, bool A8 = false>
-__global__ __launch_bounds__(NT) void k_gemm(const Params p) {
+// FUSED: a tile of the single-launch decode step (see FusedSync): GEMM1 writes
+// the down projection's input rows in the form GEMM2 reads them (bf16 rows,
+// or split: hi / lo parts, or MXFP8) with coherent stores and counts its row
+// tile in; GEMM2 starts its weight stream, waits for its row tile, reads the
+// rows with coherent loads, and writes its slot rows coherently.
+template <int FMT, bool GATED, int SPT, bool A8, bool FUSED>
+__device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, TileLds<FMT>& L,
+                                            const FusedSync& fs) {
   using C = Cfg<FMT>;
-  __shared__ __attribute__((aligned(16))) uint8_t sbuf[2][C::BUF_BYTES];
-  // MXFP4: per-wave region that rearranges a chunk's weights (2 streams x 4 steps)
-  constexpr int kWtStep = 16 * 64 + 16;
-  __shared__ __attribute__((aligned(16))) uint8_t wtr[FMT == W_MXFP4 ? NW : 1][FMT == W_MXFP4 ? 8 * kWtStep : 16];
+  constexpr int kWtStep = TileLds<FMT>::kWtStep;
+  auto& sbuf = L.sbuf;
+  auto& wtr = L.wtr;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int mt = blockIdx.x / p.n_tiles;
-  const int nt = blockIdx.x - mt * p.n_tiles;
-  if (mt >= p.status[2]) return;  // workgroup-uniform, before any barrier
+  if (mt >= __builtin_amdgcn_readfirstlane(p.status[2])) return;  // workgroup-uniform, before any barrier
   const int seg = p.tile_seg[mt];
   const int row0 = p.tile_row0[mt];
   const int rows = min(BM, p.seg_end[seg] - row0);
@@ -336,6 +435,7 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
   // weight stream needs); K past the end is zeroed when written to LDS (the
   // split rows' scale codes there are 0).
   constexpr bool QA = FMT == W_MXFP4;
+  constexpr bool COH_A = FUSED && !GATED;  // GEMM2's rows come from GEMM1 tiles of this launch
   constexpr int PPR = QA ? C::KC / 16 : C::KC / 8;  // pieces per row per chunk
   constexpr int NP = QA ? C::QPPT : C::PPT;          // pieces per thread (per array)
   constexpr int VPP = QA ? 16 : 8;                   // K values per piece
@@ -362,6 +462,14 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
     u32x4 l[QA ? NP : 1];
     u32x4 s;
   };
+  // GEMM2 of the single launch reads the rows coherently, as offsets from
+  // the split rows' base (the host keeps every offset below 2^32)
+  const uint8_t* a_base = QA ? p.Aq.hi : (const uint8_t*)p.A;
+  const __amdgpu_buffer_rsrc_t a_rs = coh_rsrc(a_base);
+  auto ld_a = [&](const void* ptr) -> u32x4 {
+    if constexpr (COH_A) return ld_coh128(a_rs, (uint32_t)((const uint8_t*)ptr - a_base));
+    else return *(const u32x4*)ptr;
+  };
   auto load_a = [&](ARegs& ar, int c) {
     const int kc = min(c * C::KC + VPP * pc, K - VPP);  // clamped: always inside the row
 #pragma unroll
@@ -370,16 +478,16 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
       if (QA) ar.l[j] = u32x4{0u, 0u, 0u, 0u};
       if (a_live[j]) {
         if (QA) {
-          ar.v[j] = *(const u32x4*)(p.Aq.hi + a_row[j] * K + kc);
-          if (!A8) ar.l[j] = *(const u32x4*)(p.Aq.lo + a_row[j] * K + kc);
+          ar.v[j] = ld_a(p.Aq.hi + a_row[j] * K + kc);
+          if (!A8) ar.l[j] = ld_a(p.Aq.lo + a_row[j] * K + kc);
         } else {
-          ar.v[j] = *(const u32x4*)(p.A + a_row[j] * K + kc);
+          ar.v[j] = ld_a(p.A + a_row[j] * K + kc);
         }
       }
     }
     // chunks past the last (the loop below loads two ahead) re-read the last
     // chunk's scale bytes: a row holds exactly 16 * nch of them
-    if (QA) ar.s = *(const u32x4*)(p.Aq.sc + s_row * p.Aq.sc_stride + 16 * min(c, nch - 1));
+    if (QA) ar.s = ld_a(p.Aq.sc + s_row * p.Aq.sc_stride + 16 * min(c, nch - 1));
   };
   auto store_a = [&](const ARegs& ar, int buf, int c) {
     const uint32_t m = c * C::KC + VPP * pc < K ? ~0u : 0u;
@@ -481,6 +589,9 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
   WSet<FMT> wx, wy;
   ARegs ar;
   load_chunk(wx, 0);
+  // GEMM2 of the single launch: the weight stream has started; now wait for
+  // the row tile's activation rows (all GEMM1 column tiles of row tile mt)
+  if constexpr (COH_A) wait_count(&fs.done1[mt], fs.n_tiles1, fs);
   load_a(ar, 0);
   if (FMT == W_MXFP4) {
 #pragma unroll
@@ -510,42 +621,91 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
   // 16x16 result layout: lane holds column (lane & 15), rows 4 (lane >> 4) + r.
   const ActParams ap = act_for(p.act, p.ep, seg);
   const float es = scale_for(GATED ? p.ep.fc1 : p.ep.fc2, seg);  // fc1 on gate and up, fc2 on down
-  if constexpr (GATED && A8) {
-    // MXFP8 activations: the down projection's input rows are quantized here,
-    // from the fp32 activation (times the route weight), with the same rule as
-    // quant_row<true>. A 32-value block of a row spans the 16 columns of two
-    // waves (w, w ^ 1): each wave reduces its magnitude over its 16 lanes,
-    // the pair exchanges the two halves through LDS. N is a multiple of 64
-    // here (the host requires I % 64 == 0), so every wave has columns.
-    __shared__ float half_amax[NW][BM];
+  if constexpr (GATED && (A8 || (FUSED && QA))) {
+    // The down projection's input rows quantized here for the block-scaled
+    // MFMA, from the activation (times the route weight), with the same rule
+    // as quant_row: MXFP8 from the fp32 value (A8), or the exact hi / lo split
+    // of its bf16 rounding (the single launch with bf16 activations). A
+    // 32-value block of a row spans the 16 columns of two waves (w, w ^ 1):
+    // each wave reduces its magnitude over its 16 lanes, the pair exchanges
+    // the two halves through LDS. N is a multiple of 64 here (the host
+    // requires I % 64 == 0), so every wave has columns.
     float v[4], m[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = q * 4 + r;
       v[r] = gated_act(ap, acc0[r] * es, acc1[r] * es) * (p.row_w && row < rows ? p.row_w[row0 + row] : 1.f);
+      if (!A8) v[r] = bf16_bits_to_f32(f32_to_bf16_rne(v[r]));
       m[r] = fabsf(v[r]);
 #pragma unroll
       for (int off = 8; off > 0; off >>= 1) m[r] = fmaxf(m[r], __shfl_xor(m[r], off));
-      if (l16 == 0) half_amax[wave][row] = m[r];
+      if (l16 == 0) L.half_amax[wave][row] = m[r];
     }
     lds_barrier();
     const int blk = (nt * block_cols(true) + wave * 16) / 32;
     const int KBo = N / 32;
+    const size_t Rq = (size_t)p.Cq.lo - (size_t)p.Cq.hi;  // rows x N bytes between the hi and lo parts
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = q * 4 + r;
-      if (row >= rows) continue;
-      const float amax = fmaxf(m[r], half_amax[wave ^ 1][row]);
-      const int code = min(max((int)((__float_as_uint(amax) >> 23) & 0xffu) - 8, 0), 254);
+      const float amax = fmaxf(m[r], L.half_amax[wave ^ 1][row]);
+      const int code = min(max((int)((__float_as_uint(amax) >> 23) & 0xffu) - (A8 ? 8 : 7), 0), 254);
       const float inv = __uint_as_float((uint32_t)(254 - code) << 23);  // 2^(127 - code)
-      const int e = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(v[r] * inv), 0.f, 0, false);
-      p.Cq.hi[(size_t)(row0 + row) * N + c0] = (uint8_t)(e & 0xff);
+      uint32_t hb, lb = 0;
+      if (A8) {
+        hb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(v[r] * inv), 0.f, 0, false) & 0xffu;
+      } else {
+        const float sv0 = v[r] * inv;
+        const int h = __builtin_amdgcn_cvt_pk_fp8_f32(sv0, 0.f, 0, false);
+        const f32x2 hf = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+        hb = (uint32_t)h & 0xffu;
+        lb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sv0 - hf[0], 0.f, 0, false) & 0xffu;
+      }
+      uint8_t* hi_row = p.Cq.hi + (size_t)(row0 + row) * N;
       uint8_t* sc_row = p.Cq.sc + (size_t)(row0 + row) * p.Cq.sc_stride;
-      if (l16 == 0 && (wave & 1) == 0) sc_row[blk] = (uint8_t)code;
-      // the row's scale bytes past its last block (up to the 16-byte padded
-      // stride) are 0, like the ones quant_row writes: GEMM2 reads them
-      if (nt == p.n_tiles - 1 && wave == 0 && KBo + l16 < p.Cq.sc_stride) sc_row[KBo + l16] = 0;
+      if (FUSED) {  // four columns per store, agent-coherent
+        const uint32_t h4 = gather4(hb), l4 = A8 ? 0u : gather4(lb);
+        if (row < rows && (l16 & 3) == 0) {
+          st_coh32(hi_row + c0, h4);
+          if (!A8) st_coh32(hi_row + Rq + c0, l4);
+        }
+        if (row < rows && l16 == 0 && (wave & 1) == 0) st_coh8(sc_row + blk, (uint32_t)code);
+        if (row < rows && nt == p.n_tiles - 1 && wave == 0 && KBo + l16 < p.Cq.sc_stride) st_coh8(sc_row + KBo + l16, 0u);
+      } else if (row < rows) {
+        hi_row[c0] = (uint8_t)hb;
+        if (!A8) hi_row[Rq + c0] = (uint8_t)lb;
+        if (l16 == 0 && (wave & 1) == 0) sc_row[blk] = (uint8_t)code;
+        // the row's scale bytes past its last block (up to the 16-byte padded
+        // stride) are 0, like the ones quant_row writes: GEMM2 reads them
+        if (nt == p.n_tiles - 1 && wave == 0 && KBo + l16 < p.Cq.sc_stride) sc_row[KBo + l16] = 0;
+      }
     }
+    if (FUSED) count_in(&fs.done1[mt]);
+    return;
+  }
+  if (FUSED) {
+    // bf16 rows out, two columns per store, agent-coherent (GEMM1: the bf16
+    // activation rows GEMM2 reads; GEMM2: the slot rows the combine reads).
+    // N is a multiple of 64, so a wave with columns has all 16 (32) of them.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = q * 4 + r;
+      uint32_t b0, b1 = 0;
+      if (GATED)
+        b0 = f32_to_bf16_rne(gated_act(ap, acc0[r] * es, acc1[r] * es) *
+                             (p.row_w && row < rows ? p.row_w[row0 + row] : 1.f));
+      else {
+        b0 = f32_to_bf16_rne(acc0[r] * es);
+        b1 = f32_to_bf16_rne(acc1[r] * es);
+      }
+      const uint32_t n0 = (uint32_t)__shfl_down((int)b0, 1), n1 = (uint32_t)__shfl_down((int)b1, 1);
+      if (wave_on && row < rows && (l16 & 1) == 0) {
+        uint16_t* dst = p.C + (size_t)(row0 + row) * N;
+        st_coh32(dst + c0, b0 | n0 << 16);
+        if (!GATED) st_coh32(dst + c1, b1 | n1 << 16);
+      }
+    }
+    count_in(GATED ? &fs.done1[mt] : fs.done2);
     return;
   }
   if (!wave_on) return;
@@ -561,6 +721,99 @@ __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
       if (c0 < N) dst[c0] = f32_to_bf16_rne(acc0[r] * es);
       if (c1 < N) dst[c1] = f32_to_bf16_rne(acc1[r] * es);
     }
+  }
+}
+
+// One tile per workgroup: blockIdx.x = row tile x column tiles + column tile.
+template <int FMT, bool GATED, int SPT, bool A8 = false>
+__global__ __launch_bounds__(NT) void k_gemm(const Params p) {
+  __shared__ TileLds<FMT> L;
+  const int mt = blockIdx.x / p.n_tiles;
+  skinny_tile<FMT, GATED, SPT, A8, false>(p, mt, blockIdx.x - mt * p.n_tiles, L, FusedSync{});
+}
+
+// The combine of the single launch: token t's slot rows, j ascending in fp32
+// (as k_combine), read with agent-coherent loads once every GEMM2 tile is in.
+struct FusedCombine {
+  const uint16_t* y;        // [rows, H] slot rows, sorted order
+  const int32_t* inv_perm;  // [T, k]
+  int32_t T, k, H;
+  uint16_t* out;            // [T, H]
+};
+
+__device__ __forceinline__ void fused_combine_token(const FusedCombine& c, int t) {
+  const int32_t* ip = c.inv_perm + (size_t)t * c.k;
+  const __amdgpu_buffer_rsrc_t y_rs = coh_rsrc(c.y);
+  for (int h = threadIdx.x * 8; h < c.H; h += NT * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < c.k; ++j) {
+      const int r = ip[j];
+      if (r < 0) continue;
+      const u32x4 v = ld_coh128(y_rs, (uint32_t)(((size_t)r * c.H + h) * 2));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += bf16_bits_to_f32(v[i] & 0xffffu);
+        acc[2 * i + 1] += bf16_bits_to_f32(v[i] >> 16);
+      }
+    }
+    u32x4 o;
+    o[0] = pack_bf16x2(acc[0], acc[1]);
+    o[1] = pack_bf16x2(acc[2], acc[3]);
+    o[2] = pack_bf16x2(acc[4], acc[5]);
+    o[3] = pack_bf16x2(acc[6], acc[7]);
+    *(u32x4*)(c.out + (size_t)t * c.H + h) = o;
+  }
+}
+
+// The single-launch decode step after the align prologue: GEMM1 tiles
+// (row-tile major), GEMM2 tiles (row-tile major), then one item per token for
+// the combine, taken from the work queue.
+template <int FMT, int SPT1, int SPT2, bool A8>
+__global__ __launch_bounds__(NT) void k_decode_fused(const Params p1, const Params p2, const FusedCombine fc,
+                                                     const FusedSync fs) {
+  __shared__ TileLds<FMT> L;
+  __shared__ int s_item;
+  const int mtl = __builtin_amdgcn_readfirstlane(p1.status[2]);
+  const int n1 = mtl * p1.n_tiles, n2 = mtl * p2.n_tiles;
+  const int total = n1 + n2 + fc.T;
+  // Wave 0 takes items from the queue, fs.batch consecutive ones at a time
+  // (lane 0 adds the batch, the others 0: lane 0's old value is the first
+  // item), and hands them to the other waves through LDS. The next batch is
+  // taken while the current one runs, so the atomic's round trip stays off
+  // the critical path; it always lies later in queue order than the current
+  // one, items run in queue order, and waits only ever point to earlier items.
+  const int B = fs.batch;
+  auto take = [&]() -> int {
+    int v = 0;
+    if (wave_id() == 0)
+      v = __hip_atomic_fetch_add(fs.queue, (threadIdx.x & 63) == 0 ? B : 0, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    return v;
+  };
+  auto publish = [&](int v) {
+    if (wave_id() == 0) s_item = __builtin_amdgcn_readfirstlane(v);
+    lds_barrier();
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
+    lds_barrier();
+    return item;
+  };
+  int first = publish(take());
+  // a workgroup takes at most every item once: the bound only guards the loop
+  for (int it = 0; it <= total && first < total; ++it) {
+    const int next = take();
+    for (int item = first; item < min(first + B, total); ++item) {
+    if (item < n1) {
+      const int mt = item / p1.n_tiles;
+      skinny_tile<FMT, true, SPT1, A8, true>(p1, mt, item - mt * p1.n_tiles, L, fs);
+    } else if (item < n1 + n2) {
+      const int i2 = item - n1, mt = i2 / p2.n_tiles;
+      skinny_tile<FMT, false, SPT2, A8, true>(p2, mt, i2 - mt * p2.n_tiles, L, fs);
+    } else {
+      wait_count(fs.done2, n2, fs);
+      fused_combine_token(fc, item - n1 - n2);
+    }
+    }
+    first = publish(next);
   }
 }
 

@@ -84,6 +84,9 @@ struct Plan {
   // byte offsets
   size_t status, counts, cu, offsets, tile_seg, tile_row0, blkcnt, blkbad, perm, inv_perm, w_sorted, xs, act,
       xq, aq, y, total;
+  size_t sync;   // single-launch decode counters: [queue, done2, -, -, done1[mt_cap]] (0 = none)
+  int n_sync;
+  bool fused;    // the forward runs the single-launch decode step
 };
 
 int check_problem(const moe_problem* p, bool grouped) {
@@ -118,6 +121,26 @@ int check_problem(const moe_problem* p, bool grouped) {
       (long long)p->I * p->H > (1LL << 30))
     return MOE_ENOTSUP;
   return MOE_OK;
+}
+
+// The single-launch decode step is taken only with MOE_EXPERTS_FUSED_DECODE=1
+// (read at every call): measured on MI355X it is slower than the separate
+// launches (align, GEMM1, activation split, GEMM2, combine), because every
+// tile must wait for its write-through hand-over stores before counting in.
+bool fused_decode_enabled() {
+  const char* e = std::getenv("MOE_EXPERTS_FUSED_DECODE");
+  return e && std::atoi(e) == 1;
+}
+
+// Items the single-launch decode step's workgroups take from its queue at a
+// time: MOE_EXPERTS_FUSED_BATCH=<n> (tuning override, n >= 1); read once.
+int fused_batch() {
+  static const int v = [] {
+    const char* e = std::getenv("MOE_EXPERTS_FUSED_BATCH");
+    const int n = e ? std::atoi(e) : 0;
+    return n > 0 ? n : 4;
+  }();
+  return v;
 }
 
 // Upper bound on GEMM2's K ranges: MOE_EXPERTS_MAX_SPLIT_K=<n> (n >= 1), read
@@ -172,6 +195,15 @@ Plan make_plan(const moe_problem& p, bool grouped, size_t ws_bytes = ~(size_t)0)
     pl.perm = take(4ull * pl.M);
     pl.inv_perm = take(4ull * pl.M);
     pl.w_sorted = take(4ull * pl.M);
+  }
+  // the single-launch decode step: weight-streaming tiles, the one-workgroup
+  // align, inputs as given (no weighted copy), K of both GEMMs <= 4096
+  const bool fused_ok =
+      !grouped && pl.skinny && pl.fused_align && !p.weight_on_input && std::max(p.H, p.I) <= 4096;
+  pl.fused = fused_ok && fused_decode_enabled();
+  if (fused_ok) {  // reserved whether or not the override turns the single launch off
+    pl.n_sync = 4 + pl.mt_cap;
+    pl.sync = take(4ull * pl.n_sync);
   }
   if (p.weight_on_input) pl.xs = take(2ull * pl.M * p.H);  // routed rows x * w, sorted order
   pl.act = take(2ull * pl.M * p.I);
@@ -324,6 +356,11 @@ int set_attrs() {
     if (e == hipSuccess)
       e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                               moe::skinny::scale_lds_bytes(moe::skinny::kMaxMxfp4K));
+  const void* fused[] = {(const void*)moe::skinny::k_decode_fused<moe::skinny::W_MXFP4, 4, 4, false>,
+                         (const void*)moe::skinny::k_decode_fused<moe::skinny::W_MXFP4, 4, 4, true>};
+  for (const void* f : fused)
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, moe::skinny::scale_lds_bytes(4096));
   if (e != hipSuccess) return MOE_EHIP;
   g_attr_done = true;
   return MOE_OK;
@@ -348,34 +385,40 @@ struct GemmIO {
 };
 
 template <bool GATED>
+moe::skinny::Params skinny_params(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws) {
+  moe::skinny::Params q;
+  q.A = (const uint16_t*)io.A;
+  q.Aq = io.Aq;
+  q.a_perm = io.a_perm;
+  q.a_div = io.a_div;
+  q.B0 = io.B0;
+  q.B1 = io.B1;
+  q.S0 = io.S0;
+  q.S1 = io.S1;
+  q.N = io.N;
+  q.K = io.K;
+  q.tile_seg = at<int32_t>(ws, pl.tile_seg);
+  q.tile_row0 = at<int32_t>(ws, pl.tile_row0);
+  q.seg_end = at<int32_t>(ws, pl.cu);
+  q.status = at<int32_t>(ws, pl.status);
+  q.mt_cap = pl.mt_cap;
+  q.n_tiles = ceil_div(io.N, moe::skinny::block_cols(GATED));
+  q.C = (uint16_t*)io.C;
+  q.Cq = io.Cq;
+  q.row_w = io.row_w;
+  q.act = act_params(p);
+  q.ep = expert_params(p);
+  return q;
+}
+
+template <bool GATED>
 int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws, hipStream_t s) {
   const int32_t* tile_seg = at<int32_t>(ws, pl.tile_seg);
   const int32_t* tile_row0 = at<int32_t>(ws, pl.tile_row0);
   const int32_t* cu = at<int32_t>(ws, pl.cu);
   const int32_t* status = at<int32_t>(ws, pl.status);
   if (pl.skinny) {
-    moe::skinny::Params q;
-    q.A = (const uint16_t*)io.A;
-    q.Aq = io.Aq;
-    q.a_perm = io.a_perm;
-    q.a_div = io.a_div;
-    q.B0 = io.B0;
-    q.B1 = io.B1;
-    q.S0 = io.S0;
-    q.S1 = io.S1;
-    q.N = io.N;
-    q.K = io.K;
-    q.tile_seg = tile_seg;
-    q.tile_row0 = tile_row0;
-    q.seg_end = cu;
-    q.status = status;
-    q.mt_cap = pl.mt_cap;
-    q.n_tiles = ceil_div(io.N, moe::skinny::block_cols(GATED));
-    q.C = (uint16_t*)io.C;
-    q.Cq = io.Cq;
-    q.row_w = io.row_w;
-    q.act = act_params(p);
-    q.ep = expert_params(p);
+    const moe::skinny::Params q = skinny_params<GATED>(p, pl, io, ws);
     const dim3 grid((unsigned)pl.mt_cap * q.n_tiles);
     const dim3 block(moe::skinny::NT);
     using moe::skinny::k_gemm;
@@ -434,6 +477,68 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
   return launch_status();
 }
 
+// Workgroups of kernel f (NT threads, dyn bytes of dynamic LDS) that fit on
+// the device at once, cached per device, kernel and LDS size.
+int resident_blocks(const void* f, size_t dyn, int* n) {
+  struct Entry {
+    int dev;
+    const void* f;
+    size_t dyn;
+    int n;
+  };
+  static Entry cache[32];
+  static int used = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].dev == dev && cache[i].f == f && cache[i].dyn == dyn) {
+      *n = cache[i].n;
+      return MOE_OK;
+    }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, moe::skinny::NT, dyn) != hipSuccess || per_cu <= 0)
+    return MOE_EHIP;
+  int rc = device_cus(&cus);
+  if (rc) return rc;
+  *n = per_cu * cus;
+  if (used < 32) cache[used++] = Entry{dev, f, dyn, *n};
+  return MOE_OK;
+}
+
+// The single-launch decode step after the align prologue: GEMM1 tiles, GEMM2
+// tiles and the combine from one work queue (gemm_skinny.hpp,
+// k_decode_fused). g1 / g2 as for the separate launches; GEMM1 writes the
+// down projection's input in the form GEMM2 reads (bf16 rows, or split for
+// the block-scaled MFMA), GEMM2 writes the slot rows y.
+int launch_fused_decode(const moe_problem& p, const Plan& pl, const GemmIO& g1, const GemmIO& g2,
+                        const int32_t* inv_perm, void* out, void* ws, hipStream_t s) {
+  using namespace moe::skinny;
+  const Params p1 = skinny_params<true>(p, pl, g1, ws);
+  const Params p2 = skinny_params<false>(p, pl, g2, ws);
+  const moe::skinny::FusedCombine fc{(const uint16_t*)g2.C, inv_perm, p.T, p.k, p.H, (uint16_t*)out};
+  int32_t* sync = at<int32_t>(ws, pl.sync);
+  const FusedSync fs{sync, sync + 4, sync + 1, at<int32_t>(ws, pl.status), p1.n_tiles, 1 << 20, fused_batch()};
+  const long long items = (long long)pl.mt_cap * (p1.n_tiles + p2.n_tiles) + p.T;
+  const bool mx = p.wfmt == MOE_W_MXFP4, mx8 = p.a_fmt == MOE_A_MXFP8;
+  const size_t dyn = mx ? (size_t)scale_lds_bytes(std::max(p.H, p.I)) : 0;
+  const void* f = mx ? (mx8 ? (const void*)k_decode_fused<W_MXFP4, 4, 4, true>
+                            : (const void*)k_decode_fused<W_MXFP4, 4, 4, false>)
+                     : (const void*)k_decode_fused<W_BF16, 0, 0, false>;
+  int cap = 0;
+  int rc = resident_blocks(f, dyn, &cap);
+  if (rc) return rc;
+  const dim3 grid((unsigned)std::max(1LL, std::min<long long>(items, cap))), block(NT);
+  if (mx && mx8)
+    hipLaunchKernelGGL((k_decode_fused<W_MXFP4, 4, 4, true>), grid, block, dyn, s, p1, p2, fc, fs);
+  else if (mx)
+    hipLaunchKernelGGL((k_decode_fused<W_MXFP4, 4, 4, false>), grid, block, dyn, s, p1, p2, fc, fs);
+  else
+    hipLaunchKernelGGL((k_decode_fused<W_BF16, 0, 0, false>), grid, block, dyn, s, p1, p2, fc, fs);
+  return launch_status();
+}
+
 int check_common_ptrs(const moe_problem* p, const void* x, const void* wg, const void* wu, const void* wd,
                       const uint8_t* sg, const uint8_t* su, const uint8_t* sd, const void* out, const void* ws) {
   if (!x || !wg || !wu || !wd || !out || !ws) return MOE_EINVAL;
@@ -461,7 +566,7 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
     if (n_ev) hipEventRecord((hipEvent_t)ev[i], s);
   };
 
-  moe::AlignOut o;
+  moe::AlignOut o{};
   o.counts = at<int32_t>(ws, pl.counts);
   o.cu = at<int32_t>(ws, pl.cu);
   o.offsets = at<int32_t>(ws, pl.offsets);
@@ -471,6 +576,10 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
   o.tile_seg = at<int32_t>(ws, pl.tile_seg);
   o.tile_row0 = at<int32_t>(ws, pl.tile_row0);
   o.status = at<int32_t>(ws, pl.status);
+  if (pl.fused) {  // the align prologue zeroes the single launch's counters
+    o.sync = at<int32_t>(ws, pl.sync);
+    o.n_sync = pl.n_sync;
+  }
   const int M = (int)pl.M;
 
   const bool mx = p->wfmt == MOE_W_MXFP4;
@@ -508,7 +617,19 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
     g1.Aq = quant_rows_at(ws, pl.xq, pl.M, p->H);
     g1.a_perm = nullptr;
   }
+  const long long y_split = pl.M * p->H;
+  GemmIO g2{at<void>(ws, pl.act), nullptr, 1, wd, nullptr, sd, nullptr, p->H, p->I, at<void>(ws, pl.y), nullptr,
+            pl.s_cap, y_split, {}, {}};
+  if (mx) g2.Aq = quant_rows_at(ws, pl.aq, pl.M, p->I);
   mark(1);
+  if (pl.fused) {  // GEMM1, GEMM2 and the combine in one launch
+    if (mx) g1.Cq = g2.Aq;  // GEMM1 writes GEMM2's split (or MXFP8) input rows directly
+    rc = launch_fused_decode(*p, pl, g1, g2, o.inv_perm, out, ws, s);
+    mark(2);
+    mark(3);
+    mark(4);
+    return rc;
+  }
   if (p->weight_on_input)
     hipLaunchKernelGGL(moe::k_scale_rows, dim3((unsigned)pl.M), dim3(256), 0, s, (const uint16_t*)x,
                        (const int32_t*)o.perm, p->k, (const float*)o.w_sorted, (const int32_t*)o.status, M, p->H,
@@ -518,11 +639,6 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
     else launch_quant(mx8, x, pl.M, p->H, g1.Aq, s, o.perm, p->k, o.status);
   }
   if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
-
-  const long long y_split = pl.M * p->H;
-  GemmIO g2{at<void>(ws, pl.act), nullptr, 1, wd, nullptr, sd, nullptr, p->H, p->I, at<void>(ws, pl.y), nullptr,
-            pl.s_cap, y_split, {}, {}};
-  if (mx) g2.Aq = quant_rows_at(ws, pl.aq, pl.M, p->I);
   mark(2);
   if (mx && !mx8) launch_quant(false, g2.A, pl.M, p->I, g2.Aq, s);
   if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
@@ -560,6 +676,7 @@ int moe_experts_workspace_layout(const moe_problem* p, moe_ws_layout* l) {
   l->xq = pl.xq;
   l->xq_rows = pl.xq ? (size_t)(pl.fused_align && !p->weight_on_input ? p->T : pl.M) : 0;
   l->aq = pl.aq;
+  l->single_launch = pl.fused ? 1 : 0;
   return MOE_OK;
 }
 
@@ -623,7 +740,7 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t*
   const Plan pl = make_plan(p, false);
   if (workspace_bytes < pl.perm) return MOE_ENOSPC;
   if ((rc = set_attrs())) return rc;
-  moe::AlignOut o;
+  moe::AlignOut o{};
   o.counts = counts;
   o.cu = cu_seqlens;
   o.offsets = at<int32_t>(workspace, pl.offsets);
@@ -771,9 +888,13 @@ int moe_route(const moe_route_problem* p, const float* logits, const float* bias
 
 int moe_device_error(const void* workspace, int32_t* n_bad) {
   if (!workspace || !n_bad) return MOE_EINVAL;
-  // status word sits at offset 0 of every workspace layout
-  const hipError_t e = hipMemcpy(n_bad, workspace, sizeof(int32_t), hipMemcpyDeviceToHost);
-  return e == hipSuccess ? MOE_OK : MOE_EHIP;
+  // status words sit at offset 0 of every workspace layout: [0] bad ids,
+  // [3] a single-launch wait gave up
+  int32_t st[4] = {0, 0, 0, 0};
+  const hipError_t e = hipMemcpy(st, workspace, sizeof(st), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return MOE_EHIP;
+  *n_bad = st[0];
+  return st[3] ? MOE_ETIMEDOUT : MOE_OK;
 }
 
 int moe_check_expert_params(const moe_problem* p, const float* alpha_e, const float* beta_e,
@@ -804,6 +925,7 @@ const char* moe_strerror(int status) {
     case MOE_ENOTSUP: return "unsupported problem";
     case MOE_ENOSPC: return "workspace too small";
     case MOE_EHIP: return "HIP error";
+    case MOE_ETIMEDOUT: return "a wait on the device gave up";
     default: return "unknown status";
   }
 }

@@ -161,6 +161,18 @@ typedef struct {
                            events 2, 3 and 4 together after it; act is not written with MXFP4
                            weights (GEMM1 writes the split rows in aq). The workspace holds
                            its counters either way. */
+  size_t mx_tiled;   /* 1 when MXFP4 weights with MXFP8 activations run the LDS-tiled
+                        block-scaled kernels (more than 32 rows per expert on average,
+                        unless MOE_EXPERTS_MX_PREFILL=0 at the call). Then xq holds the
+                        token rows (xq_rows = T; T*k sorted rows with the route weight on
+                        the input) in the split layout above with no lo part used, and
+                        aq holds only the e4m3 activation codes, T*k rows of I bytes in
+                        sorted row order, their scales in aq_sc. */
+  size_t aq_sc;      /* mx_tiled: e8m0 scales of the activation rows, per 256-row tile t
+                        (the align's tiles of each segment, in segment order) and
+                        128-column group g: a 1 KB block at aq_sc + (t * ceil(I/128) + g)
+                        * 1024, 4 bytes per tile row holding the scales of its column
+                        blocks 4g, 4g+2, 4g+1, 4g+3 in that order (0 past I / 32) */
 } moe_ws_layout;
 
 /* Workspace bytes a moe_experts_forward call on problem *p needs (0 if *p is

@@ -54,7 +54,7 @@ class MoeRouteProblem(ctypes.Structure):
 class MoeWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("status", "counts", "cu_seqlens", "perm", "inv_perm", "w_sorted", "act", "y", "total",
-                 "xq", "xq_rows", "aq", "single_launch")]
+                 "xq", "xq_rows", "aq", "single_launch", "mx_tiled", "aq_sc")]
 
 
 class MoeError(RuntimeError):

@@ -105,12 +105,69 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
+// Epilogue of a wave's 128 x 64 block of 32x32 MFMA results (GEMM1: gate
+// results in acc[i][0], up in acc[i][1], for the same 128 x 32 outputs).
+// 32x32 result layout: lane holds column (lane & 31) and, in register r, row
+// 8 (r / 4) + 4 (lane / 32) + (r % 4) of the 32-row block i. Results go
+// through the wave's own 16 KB of LDS (free once every wave has finished its
+// operand reads) so that every lane stores 16 contiguous bytes: 128 rows x 32
+// columns per pass, rows padded to 40 elements against bank conflicts.
+// GEMM1 writes act = f(gate * es, up * es) * route weight; GEMM2 down * es.
+// wrows: rows of the block inside the segment; wrow0: first output row;
+// col0: first output column.
+template <bool GATED>
+__device__ __forceinline__ void store_block_bf16(const f32x16 (&acc)[4][2], lds_u32x4* smem, int wave, int wrows,
+                                                 int wrow0, int col0, int N, uint16_t* __restrict__ Cs,
+                                                 const float* row_w, const ActParams& ap, float es) {
+  constexpr int LDR = 40;
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, lk = lane >> 5;
+  lds_u16* sc = (lds_u16*)&smem[wave * 1024];
+  const int cc = lane & 3;  // 16-byte chunk of a staged 64-byte row
+  const int rr = lane >> 2; // staged row within a group of 16
+#pragma unroll
+  for (int pass = 0; pass < (GATED ? 1 : 2); ++pass) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int rbase = i * 32 + rq * 8 + lk * 4;  // 4 consecutive rows r = rq*4 + 0..3
+        float w4[4] = {1.f, 1.f, 1.f, 1.f};
+        if (GATED) {
+#pragma unroll
+          for (int r3 = 0; r3 < 4; ++r3)
+            if (row_w && rbase + r3 < wrows) w4[r3] = row_w[wrow0 + rbase + r3];
+        }
+#pragma unroll
+        for (int r3 = 0; r3 < 4; ++r3) {
+          const int r = rq * 4 + r3;
+          float v;
+          if (GATED) v = gated_act(ap, acc[i][0][r] * es, acc[i][1][r] * es) * w4[r3];
+          else v = acc[i][pass][r] * es;
+          const __bf16 h = (__bf16)v;
+          sc[(rbase + r3) * LDR + lr] = *(const uint16_t*)&h;
+        }
+      }
+    }
+    const int c = col0 + pass * 32 + cc * 8;
+    if (c < N) {
+#pragma unroll 4
+      for (int t = 0; t < 8; ++t) {
+        const int row = t * 16 + rr;
+        if (row < wrows)
+          *(u32x4*)(Cs + (size_t)(wrow0 + row) * N + c) = *(const lds_u32x4*)&sc[row * LDR + cc * 8];
+      }
+    }
+  }
+}
+
 // Work item -> (row tile, column tile, K range). Items: groups of gn column
 // tiles, row tiles inside a group, column tile fastest, K range fastest of
 // all (GEMM2 may split K into nsplit ranges when there are too few tiles to
 // fill the last round; each range writes its own partial output, summed by
 // the combine).
-__device__ __forceinline__ void item_tile(const Params& p, int item, int mtl, int nsplit, int& mt, int& nt,
+template <class P>
+__device__ __forceinline__ void item_tile(const P& p, int item, int mtl, int nsplit, int& mt, int& nt,
                                           int& split) {
   split = item % nsplit;
   const int tl = item / nsplit;
@@ -322,56 +379,12 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int mt, int nt, int s
   wait_vmcnt<0>();
   stage_barrier();
 
-  // ---- epilogue. 32x32 result layout: lane holds column (lane & 31) and, in
-  // register r, row 8 (r / 4) + 4 (lane / 32) + (r % 4).
+  // ---- epilogue
   if (!active) return;
-  // Results go through LDS so that every lane stores 16 contiguous bytes;
-  // each wave stages in its own 16 KB of the (now free) stage buffers.
-  // 128 rows x 32 columns per pass, rows padded to 40 elements against bank
-  // conflicts.
-  constexpr int LDR = 40;
-  lds_u16* sc = (lds_u16*)&smem[wave * 1024];
-  const int wrows = min(128, rows - wm * 128);
-  uint16_t* __restrict__ Cs = p.C + (size_t)split * p.c_split;
-  const int wrow0 = row0 + wm * 128;
-  const ActParams ap = act_for(p.act, p.ep, seg);
-  const float es = scale_for(GATED ? p.ep.fc1 : p.ep.fc2, seg);  // fc1 on gate and up, fc2 on down
-  const int cc = lane & 3;          // 16-byte chunk of a staged 64-byte row
-  const int rr = lane >> 2;         // staged row within a group of 16
-#pragma unroll
-  for (int pass = 0; pass < (GATED ? 1 : 2); ++pass) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int rbase = i * 32 + rq * 8 + lk * 4;  // 4 consecutive rows r = rq*4 + 0..3
-        float w4[4] = {1.f, 1.f, 1.f, 1.f};
-        if (GATED) {
-#pragma unroll
-          for (int r3 = 0; r3 < 4; ++r3)
-            if (p.row_w && rbase + r3 < wrows) w4[r3] = p.row_w[wrow0 + rbase + r3];
-        }
-#pragma unroll
-        for (int r3 = 0; r3 < 4; ++r3) {
-          const int r = rq * 4 + r3;
-          float v;
-          if (GATED) v = gated_act(ap, acc[i][0][r] * es, acc[i][1][r] * es) * w4[r3];
-          else v = acc[i][pass][r] * es;
-          const __bf16 h = (__bf16)v;
-          sc[(rbase + r3) * LDR + lr] = *(const uint16_t*)&h;
-        }
-      }
-    }
-    const int col0 = n0 + (GATED ? wn * 32 : wn * 64 + pass * 32) + cc * 8;
-    if (col0 < N) {
-#pragma unroll 4
-      for (int t = 0; t < 8; ++t) {
-        const int row = t * 16 + rr;
-        if (row < wrows)
-          *(u32x4*)(Cs + (size_t)(wrow0 + row) * N + col0) = *(const lds_u32x4*)&sc[row * LDR + cc * 8];
-      }
-    }
-  }
+  store_block_bf16<GATED>(acc, smem, wave, min(128, rows - wm * 128), row0 + wm * 128,
+                          n0 + (GATED ? wn * 32 : wn * 64), p.N, p.C + (size_t)split * p.c_split,
+                          GATED ? p.row_w : nullptr, act_for(p.act, p.ep, seg),
+                          scale_for(GATED ? p.ep.fc1 : p.ep.fc2, seg));  // fc1 on gate and up, fc2 on down
 }
 
 // Only the device knows the number of row tiles, so the grid covers an upper

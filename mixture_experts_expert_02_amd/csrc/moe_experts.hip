@@ -19,6 +19,7 @@
 #include "combine.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_skinny.hpp"
+#include "gemm_mx.hpp"
 #include "decode_prologue.hpp"
 #include "router.hpp"
 #include "scale_rows.hpp"
@@ -67,8 +68,19 @@ int bits_for(int E) {  // bits needed for keys 0..E
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Decode-shaped problems (few rows per weight row) and all MXFP4 problems use
-// the weight-streaming kernels; the rest the LDS-tiled MFMA kernels.
+// MXFP4 weights with MXFP8 activations and more than 32 rows per expert on
+// average (token-major entry): the LDS-tiled block-scaled kernels of
+// gemm_mx.hpp. MOE_EXPERTS_MX_PREFILL=0 (read at every call) sends these
+// problems to the weight-streaming kernels instead (tests compare the two).
+bool use_mxbig(const moe_problem& p, long long rows, bool grouped) {
+  if (grouped || p.wfmt != MOE_W_MXFP4 || p.a_fmt != MOE_A_MXFP8 || rows <= 32LL * p.E) return false;
+  const char* e = std::getenv("MOE_EXPERTS_MX_PREFILL");
+  return !(e && std::atoi(e) == 0);
+}
+
+// Decode-shaped problems (few rows per weight row) and the other MXFP4
+// problems use the weight-streaming kernels; the rest the LDS-tiled MFMA
+// kernels.
 bool use_skinny(const moe_problem& p, long long rows) {
   return p.wfmt == MOE_W_MXFP4 || rows <= 32LL * p.E;
 }
@@ -87,6 +99,12 @@ struct Plan {
   size_t sync;   // single-launch decode counters: [queue, done2, -, -, done1[mt_cap]] (0 = none)
   int n_sync;
   bool fused;    // the forward runs the single-launch decode step
+  // LDS-tiled MXFP4 x MXFP8 kernels: scale blocks of GEMM1's A (sa1) and
+  // GEMM2's A (sa2, written by GEMM1), of the weights (ws1, ws2); column
+  // tiles and 128-K stages of each GEMM
+  bool mxbig;
+  size_t sa1, sa2, ws1, ws2;
+  int NT1, KT1, NT2, KT2;
 };
 
 int check_problem(const moe_problem* p, bool grouped) {
@@ -161,15 +179,22 @@ size_t quant_bytes(long long R, int K) {
 Plan make_plan(const moe_problem& p, bool grouped, size_t ws_bytes = ~(size_t)0) {
   Plan pl{};
   pl.M = grouped ? (long long)p.T : (long long)p.T * p.k;
-  pl.skinny = use_skinny(p, pl.M);
-  pl.BM = pl.skinny ? moe::skinny::BM : moe::big::BM;
+  pl.mxbig = use_mxbig(p, pl.M, grouped);
+  pl.skinny = !pl.mxbig && use_skinny(p, pl.M);
+  pl.BM = pl.skinny ? moe::skinny::BM : pl.mxbig ? moe::mx::BM : moe::big::BM;
+  if (pl.mxbig) {
+    pl.NT1 = ceil_div(p.I, moe::mx::BN / 2);
+    pl.KT1 = ceil_div(p.H, moe::mx::BK);
+    pl.NT2 = ceil_div(p.H, moe::mx::BN);
+    pl.KT2 = ceil_div(p.I, moe::mx::BK);
+  }
   pl.mt_cap = ceil_div(pl.M, pl.BM) + (int)std::min<long long>(p.E, pl.M);
   // Splitting GEMM2's K only pays when its tiles fill a few rounds of the
   // compute units at most; with up to 1024 tiles (four rounds of 256 units)
   // room is kept for four partial outputs.
   pl.s_cap = 1;
   if (!grouped && !pl.skinny && (long long)pl.mt_cap * ceil_div(p.H, moe::big::BN) <= 1024)
-    pl.s_cap = std::max(1, std::min(max_split_k(), p.I / moe::big::BK));
+    pl.s_cap = std::max(1, std::min(max_split_k(), pl.mxbig ? pl.KT2 : p.I / moe::big::BK));
   pl.fused_align = !grouped && pl.M <= kFusedMaxRows && p.E <= kFusedMaxExperts;
   if (!grouped && !pl.fused_align) {
     pl.chunk = (int)std::max<long long>(512, (ceil_div(pl.M, 256) + 63) / 64 * 64);
@@ -206,10 +231,22 @@ Plan make_plan(const moe_problem& p, bool grouped, size_t ws_bytes = ~(size_t)0)
     pl.sync = take(4ull * pl.n_sync);
   }
   if (p.weight_on_input) pl.xs = take(2ull * pl.M * p.H);  // routed rows x * w, sorted order
-  pl.act = take(2ull * pl.M * p.I);
-  if (p.wfmt == MOE_W_MXFP4) {  // activation rows split for the block-scaled MFMA, sorted order
-    pl.xq = take(quant_bytes(pl.M, p.H));
-    pl.aq = take(quant_bytes(pl.M, p.I));
+  if (pl.mxbig) {
+    // x rows quantized in token order (the weighted copies in sorted order),
+    // GEMM2's input codes in sorted order, the scale blocks
+    const size_t blk = moe::mx::SC_BYTES;
+    pl.xq = take(quant_bytes(p.weight_on_input ? pl.M : (long long)p.T, p.H));
+    pl.sa1 = take(blk * pl.mt_cap * pl.KT1);
+    pl.aq = take((size_t)pl.M * p.I);
+    pl.sa2 = take(blk * pl.mt_cap * pl.NT1);
+    pl.ws1 = take(blk * p.E * pl.NT1 * pl.KT1);
+    pl.ws2 = take(blk * p.E * pl.NT2 * pl.KT2);
+  } else {
+    pl.act = take(2ull * pl.M * p.I);
+    if (p.wfmt == MOE_W_MXFP4) {  // activation rows split for the block-scaled MFMA, sorted order
+      pl.xq = take(quant_bytes(pl.M, p.H));
+      pl.aq = take(quant_bytes(pl.M, p.I));
+    }
   }
   if (!grouped) {
     pl.y = o;
@@ -539,6 +576,118 @@ int launch_fused_decode(const moe_problem& p, const Plan& pl, const GemmIO& g1, 
   return launch_status();
 }
 
+// Token-major forward on the LDS-tiled MXFP4 x MXFP8 kernels, after the
+// align: x rows quantized (k_quant_rows), scale blocks prepared (k_mx_prep),
+// GEMM1 (its epilogue quantizes GEMM2's input), GEMM2, combine.
+template <class Mark>
+int forward_mx(const moe_problem& p, const Plan& pl, const void* x, const moe::AlignOut& o, const void* wg,
+               const void* wu, const void* wd, const uint8_t* sg, const uint8_t* su, const uint8_t* sd, void* out,
+               void* ws, hipStream_t s, Mark&& mark) {
+  const int M = (int)pl.M;
+  const long long R = p.weight_on_input ? pl.M : (long long)p.T;
+  const moe::skinny::QRows xq = quant_rows_at(ws, pl.xq, R, p.H);
+  if (p.weight_on_input) {  // rows x * w in sorted order, quantized in that order
+    hipLaunchKernelGGL(moe::k_scale_rows, dim3((unsigned)pl.M), dim3(256), 0, s, (const uint16_t*)x,
+                       (const int32_t*)o.perm, p.k, (const float*)o.w_sorted, (const int32_t*)o.status, M, p.H,
+                       at<uint16_t>(ws, pl.xs));
+    launch_quant(true, at<void>(ws, pl.xs), R, p.H, xq, s);
+  } else {
+    launch_quant(true, x, R, p.H, xq, s);
+  }
+  moe::mx::PrepParams pp;
+  pp.Sg = sg;
+  pp.Su = su;
+  pp.Sd = sd;
+  pp.WS1 = at<uint8_t>(ws, pl.ws1);
+  pp.WS2 = at<uint8_t>(ws, pl.ws2);
+  pp.E = p.E;
+  pp.H = p.H;
+  pp.I = p.I;
+  pp.NT1 = pl.NT1;
+  pp.KT1 = pl.KT1;
+  pp.NT2 = pl.NT2;
+  pp.KT2 = pl.KT2;
+  pp.counts = o.counts;
+  pp.xs = xq.sc;
+  pp.xs_stride = xq.sc_stride;
+  pp.perm = p.weight_on_input ? nullptr : o.perm;
+  pp.div = p.k;
+  pp.tile_seg = o.tile_seg;
+  pp.tile_row0 = o.tile_row0;
+  pp.seg_end = o.cu;
+  pp.status = o.status;
+  pp.mt_cap = pl.mt_cap;
+  pp.SA1 = at<uint8_t>(ws, pl.sa1);
+  const long long nprep = (long long)p.E * (pl.NT1 + pl.NT2) + pl.mt_cap;
+  if (nprep > 0x7fffffffLL) return MOE_ENOTSUP;
+  hipLaunchKernelGGL(moe::mx::k_mx_prep, dim3((unsigned)nprep), dim3(256), 0, s, pp);
+
+  int ncu = 0;
+  int rc = device_cus(&ncu);
+  if (rc) return rc;
+  moe::mx::Params g{};
+  g.A = xq.hi;
+  g.a_bytes = (uint32_t)(R * p.H);
+  g.a_perm = p.weight_on_input ? nullptr : o.perm;
+  g.a_div = p.k;
+  g.A_sc = pp.SA1;
+  g.B0 = (const uint8_t*)wg;
+  g.B1 = (const uint8_t*)wu;
+  g.B_sc = pp.WS1;
+  g.N = p.I;
+  g.K = p.H;
+  g.KT = pl.KT1;
+  g.tile_seg = o.tile_seg;
+  g.tile_row0 = o.tile_row0;
+  g.seg_end = o.cu;
+  g.status = o.status;
+  g.mt_cap = pl.mt_cap;
+  g.n_tiles = pl.NT1;
+  g.gn = std::min(pl.NT1, group_cols_override() ? group_cols_override() : 2);
+  g.s_cap = 1;
+  g.ncu = ncu;
+  g.Cq = at<uint8_t>(ws, pl.aq);
+  g.Cq_sc = at<uint8_t>(ws, pl.sa2);
+  g.row_w = p.weight_on_input ? nullptr : o.w_sorted;
+  g.act = act_params(p);
+  g.ep = expert_params(p);
+  long long nblk = ((long long)pl.mt_cap * pl.NT1 + 7) / 8 * 8;
+  if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
+  hipLaunchKernelGGL(moe::mx::k_gemm<true>, dim3((unsigned)nblk), dim3(moe::mx::NT), 0, s, g);
+  if ((rc = launch_status())) return rc;
+  mark(2);
+
+  moe::mx::Params g2 = g;
+  g2.A = at<uint8_t>(ws, pl.aq);
+  g2.a_bytes = (uint32_t)((long long)M * p.I);
+  g2.a_perm = nullptr;
+  g2.A_sc = g.Cq_sc;
+  g2.B0 = (const uint8_t*)wd;
+  g2.B1 = nullptr;
+  g2.B_sc = at<uint8_t>(ws, pl.ws2);
+  g2.N = p.H;
+  g2.K = p.I;
+  g2.KT = pl.KT2;
+  g2.n_tiles = pl.NT2;
+  g2.gn = std::min(pl.NT2, group_cols_override() ? group_cols_override() : 2);
+  g2.s_cap = pl.s_cap;
+  g2.c_split = pl.M * p.H;
+  g2.C = at<uint16_t>(ws, pl.y);
+  g2.Cq = nullptr;
+  g2.Cq_sc = nullptr;
+  g2.row_w = nullptr;
+  nblk = ((long long)pl.mt_cap * pl.NT2 * pl.s_cap + 7) / 8 * 8;
+  if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
+  hipLaunchKernelGGL(moe::mx::k_gemm<false>, dim3((unsigned)nblk), dim3(moe::mx::NT), 0, s, g2);
+  if ((rc = launch_status())) return rc;
+  mark(3);
+  moe::SplitSum ss{o.status, pl.NT2, pl.KT2, ncu, pl.s_cap, pl.M * p.H};
+  hipLaunchKernelGGL(moe::k_combine, dim3(p.T, ceil_div(p.H, 256 * 8)), dim3(256), 0, s, at<const uint16_t>(ws, pl.y),
+                     (const int32_t*)o.inv_perm, p.T, p.k, p.H, ss, (uint16_t*)out);
+  mark(4);
+  return launch_status();
+}
+
 int check_common_ptrs(const moe_problem* p, const void* x, const void* wg, const void* wu, const void* wd,
                       const uint8_t* sg, const uint8_t* su, const uint8_t* sd, const void* out, const void* ws) {
   if (!x || !wg || !wu || !wd || !out || !ws) return MOE_EINVAL;
@@ -586,7 +735,7 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
   const bool mx8 = p->a_fmt == MOE_A_MXFP8;
   // MXFP4 with the one-workgroup align: x split in token order in the same
   // launch (GEMM1 reads it through the permutation)
-  const bool mx_prologue = mx && pl.fused_align && !p->weight_on_input;
+  const bool mx_prologue = mx && pl.fused_align && !p->weight_on_input && !pl.mxbig;
   mark(0);
   if (mx_prologue) {
     const size_t lds = (size_t)(7 * p->E + 16) * 4;
@@ -603,6 +752,10 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
     return rc;
   }
 
+  if (pl.mxbig) {
+    mark(1);
+    return forward_mx(*p, pl, x, o, wg, wu, wd, sg, su, sd, out, ws, s, mark);
+  }
   GemmIO g1{x, o.perm, p->k, wg, wu, sg, su, p->I, p->H, at<void>(ws, pl.act), o.w_sorted, 1, 0, {}, {}};
   // MXFP8 activations: GEMM1's epilogue quantizes the activation rows for GEMM2 itself
   if (mx8) g1.Cq = quant_rows_at(ws, pl.aq, pl.M, p->I);
@@ -674,9 +827,11 @@ int moe_experts_workspace_layout(const moe_problem* p, moe_ws_layout* l) {
   l->y = pl.y;
   l->total = pl.total;
   l->xq = pl.xq;
-  l->xq_rows = pl.xq ? (size_t)(pl.fused_align && !p->weight_on_input ? p->T : pl.M) : 0;
+  l->xq_rows = pl.xq ? (size_t)((pl.fused_align || pl.mxbig) && !p->weight_on_input ? p->T : pl.M) : 0;
   l->aq = pl.aq;
   l->single_launch = pl.fused ? 1 : 0;
+  l->mx_tiled = pl.mxbig ? 1 : 0;
+  l->aq_sc = pl.mxbig ? pl.sa2 : 0;
   return MOE_OK;
 }
 

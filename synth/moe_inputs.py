@@ -53,6 +53,7 @@ class Workload:
     n_empty_real: int = 0            # pre-grouped: real experts left empty
     n_used_slots: int = 0            # pre-grouped: redundant slots that hold rows
     wid: int = 0                     # workload id mixed into every seed
+    act_fmt: str = "bf16"            # "bf16" | "mxfp8" (GEMM inputs as MXFP8, MXFP4 weights only)
 
     @property
     def M(self) -> int:
@@ -75,6 +76,11 @@ WORKLOADS = {
     # Decode with MXFP4 weights and clamped SwiGLU-OAI (alpha 1.702, limit 7, beta 1).
     "mxfp4_decode": Workload("mxfp4_decode", T=32, H=2880, I=2880, E=128, k=4, wfmt="mxfp4",
                              act="swiglu_oai", alpha=1.702, beta=1.0, limit=7.0, wid=4),
+    # Prefill with MXFP4 weights and MXFP8 activations: the decode layer's
+    # shapes (H=I=2880, E=128, top-4, clamped SwiGLU-OAI) at 8192 tokens,
+    # 256 routed rows per expert on average.
+    "mxfp4_prefill": Workload("mxfp4_prefill", T=8192, H=2880, I=2880, E=128, k=4, wfmt="mxfp4",
+                              act="swiglu_oai", alpha=1.702, beta=1.0, limit=7.0, act_fmt="mxfp8", wid=6),
     # Pre-grouped redundant-slot layout: 32 experts + 8 slots, NvS=16384.
     "pregrouped": Workload("pregrouped", T=16384, H=7168, I=2048, E=40, k=1, pregrouped=True,
                            n_real=32, n_empty_real=2, n_used_slots=3, zipf_s=1.2, wid=5),

@@ -68,7 +68,10 @@ def sampled_token_oracle(x, ids, w, wg, wu, wd, tokens, act_kw=None, mx=False):
 
 
 def wl_act_kw(wl):
-    return dict(act=wl.act, alpha=wl.alpha, beta=wl.beta, limit=wl.limit)
+    kw = dict(act=wl.act, alpha=wl.alpha, beta=wl.beta, limit=wl.limit)
+    if wl.act_fmt != "bf16":
+        kw["act_fmt"] = wl.act_fmt
+    return kw
 
 
 class Guarded:
@@ -98,3 +101,129 @@ class Guarded:
     def view_bf16(self, *shape):
         n = int(np.prod(shape))
         return self.body[: 2 * n].view(torch.bfloat16).view(*shape)
+
+
+def _quantize_with_codes(a, codes):
+    """MXFP8 values of rows `a` with the given e8m0 scale code per 32-block."""
+    R, K = a.shape
+    X = np.ldexp(1.0, codes.astype(np.int64) - 127)[..., None]
+    return (oracle.e4m3_round(a.reshape(R, K // 32, 32) / X) * X).reshape(R, K)
+
+
+def mxfp8_activation_bounds(x, ids, w, W, S, act_kw, kernel_err_factor=1.0):
+    """The down projection's input rows of the MXFP8 path in sorted row
+    order, as the oracle computes them (float64, before quantization), and a
+    bound d on how far the kernels' fp32 value of each element may lie from
+    it: GEMM1's products are exact in fp32, so each dot product over K terms
+    is off by at most K * 2^-24 * sum |x_i w_i| (the standard bound of fp32
+    summation in any order; times kernel_err_factor), and d is the largest
+    change of f(g, u) * route weight over the corners of that box, plus
+    eight fp32 roundings of the result.
+
+    Returns (al, a, d, D_of): the oracle's align, a and d [valid rows, I],
+    and D_of(e) the expert's down matrix."""
+    T, k = ids.shape
+    Wn = [(c.numpy(), s.numpy()) for c, s in zip(W, S)]
+    E = Wn[0][0].shape[0]
+    par = {kk: v for kk, v in act_kw.items() if kk in ("alpha", "beta", "limit")}
+    act = act_kw.get("act", "silu")
+    al = oracle.align(ids, E)
+    cu = al["cu_seqlens"]
+    nv = int(cu[-1])
+    I = Wn[0][0].shape[1]
+    xq = oracle.mxfp8_quantize(to_np(x).astype(np.float64))[0]
+    a_all = np.zeros((nv, I))
+    d_all = np.zeros((nv, I))
+    u_ = 2.0 ** -24
+    start = 0
+    for e in range(E):
+        end = int(cu[e])
+        if end == start:
+            continue
+        rows = al["perm"][start:end]
+        wr = w.reshape(-1)[rows][:, None].astype(np.float64)
+        if act_kw.get("weight_on_input"):
+            # route weight on the input: weighted token rows, rounded to bf16,
+            # quantized; the activation carries no weight
+            xr = oracle.mxfp8_quantize(oracle.bf16_round(to_np(x).astype(np.float64)[rows // k] * wr))[0]
+            wr = np.ones_like(wr)
+        else:
+            xr = xq[rows // k]
+        G, U = (oracle.expert_matrix(Wn[i], e) for i in range(2))
+        g, u = xr @ G.T, xr @ U.T
+        Kg = xr.shape[1]
+        dg = kernel_err_factor * Kg * u_ * (np.abs(xr) @ np.abs(G).T)
+        du = kernel_err_factor * Kg * u_ * (np.abs(xr) @ np.abs(U).T)
+        a = oracle.activation(act, g, u, **par) * wr
+        da = np.zeros_like(a)
+        for sg in (-1.0, 1.0):
+            for su in (-1.0, 1.0):
+                da = np.maximum(da, np.abs(oracle.activation(act, g + sg * dg, u + su * du, **par) * wr - a))
+        a_all[start:end] = a
+        d_all[start:end] = da + 8 * u_ * np.abs(a)
+        start = end
+    return al, a_all, d_all, lambda e: oracle.expert_matrix(Wn[2], e)
+
+
+def mxfp8_extremes(a, d):
+    """The element values of smallest and largest magnitude within d of a."""
+    return np.sign(a) * np.maximum(np.abs(a) - d, 0.0), np.sign(a) * (np.abs(a) + d)
+
+
+def mxfp8_reference_with_envelope(x, ids, w, W, S, act_kw, kernel_err_factor=1.0):
+    """Oracle output of the MXFP8 path and an elementwise envelope for the
+    quantization decisions the kernels may take the other way.
+
+    The MXFP8 rounding of an activation element (e4m3 rounds to nearest, one
+    step is 1/16 to 1/8 of the value) and its block's scale code (from the
+    block's largest magnitude) are both fixed by values in [a - d, a + d]
+    (mxfp8_activation_bounds); where that interval holds a rounding midpoint
+    or a power of two the kernels may take either decision, and both are
+    correct to the kernels' precision. The envelope is the largest change of
+    the down projection's output those elements can make (their largest
+    change of quantized value times |W_down|), summed over a token's slots;
+    it is 0 wherever every decision is fixed.
+
+    Returns (ref, envelope, n_ambiguous_elements)."""
+    T, k = ids.shape
+    H = x.shape[1]
+    al, a, d, D_of = mxfp8_activation_bounds(x, ids, w, W, S, act_kw, kernel_err_factor)
+    cu = al["cu_seqlens"]
+    q, _, codes = oracle.mxfp8_quantize(a)
+    small, big = mxfp8_extremes(a, d)
+    dev = np.zeros_like(a)
+    for c in (codes, oracle.mxfp8_quantize(small)[2], oracle.mxfp8_quantize(big)[2]):
+        for v in (small, big):
+            dev = np.maximum(dev, np.abs(_quantize_with_codes(v, c) - q))
+    M = T * k
+    y = np.zeros((M, H))
+    env = np.zeros((M, H))
+    start = 0
+    for e in range(len(cu)):
+        end = int(cu[e])
+        if end == start:
+            continue
+        D = D_of(e)
+        y[start:end] = q[start:end] @ D.T
+        env[start:end] = dev[start:end] @ np.abs(D).T
+        start = end
+    inv = al["inv_perm"].reshape(T, k)
+    out = np.zeros((T, H))
+    out_env = np.zeros((T, H))
+    for j in range(k):
+        r = inv[:, j]
+        ok = r >= 0
+        out[ok] += y[r[ok]]
+        out_env[ok] += env[r[ok]]
+    return out, out_env, int(np.count_nonzero(dev))
+
+
+def check_mxfp8_output(got, ref, env, tol=TOL):
+    """|got - ref| <= tol * max|ref| + env elementwise; returns (plain rel
+    error, rel error beyond the envelope, outputs that needed the envelope)."""
+    got = np.asarray(got, dtype=np.float64)
+    scale = np.abs(ref).max()
+    d = np.abs(got - ref)
+    beyond = np.maximum(d - env, 0.0)
+    used = int(np.count_nonzero((d > tol * scale) & (d <= tol * scale + env)))
+    return float(d.max() / scale), float(beyond.max() / scale), used

@@ -8,9 +8,11 @@ The metric has two halves: bf16 prefill TFLOP/s and MXFP4 decode weight-stream
 GB/s. The default run (--workload all) measures four workloads one after the
 other and puts the headline on the largest, the fine-grained prefill layer
 (T=8192, H=7168, I=2048, E=256 resident experts, top-8, Zipf-skewed load);
-the Mixtral-shaped prefill, the MXFP4 decode step and the pre-grouped layout
-go into the same line under "configs", each with its step time, value,
-roofline and CPU-oracle baseline.
+the Mixtral-shaped prefill, the MXFP4 decode step, the pre-grouped layout
+and the MXFP4-weight prefill with MXFP8 activations (the decode layer's
+shapes at 8192 tokens, on the block-scaled MFMA, roofline against the fp8
+peak) go into the same line under "configs", each with its step time,
+value, roofline and CPU-oracle baseline.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|NAME]
                   [--no-cpu-baseline] [--calib-copy] [--router] [--act-fmt bf16|mxfp8]
@@ -37,11 +39,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (MXFP8 x MXFP4 block-scaled MFMAs run at this rate)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 STAGES = ("align", "gemm1", "gemm2", "combine")
 METRIC = "MoE experts TFLOP/s (bf16 prefill) + weight-stream GB/s (MXFP4 decode), 1 GPU"
 HEADLINE = "fine_grained_prefill"
-NESTED = ("mixtral_prefill", "mxfp4_decode", "pregrouped")
+NESTED = ("mixtral_prefill", "mxfp4_decode", "pregrouped", "mxfp4_prefill")
 DECODE_MIN_STEPS = 200      # a 0.2 ms step: fewer steps let the timed region's ends show
 
 
@@ -60,8 +63,9 @@ def parse():
     ap.add_argument("--print-source-hash", action="store_true")
     ap.add_argument("--router", action="store_true",
                     help="run the router (moe_route, Renormalize) on the workload's logits inside each step")
-    ap.add_argument("--act-fmt", default="bf16", choices=("bf16", "mxfp8"),
-                    help="activation format of the GEMM inputs (mxfp8: MXFP4-weight workloads only)")
+    ap.add_argument("--act-fmt", default=None, choices=("bf16", "mxfp8"),
+                    help="activation format of the GEMM inputs (mxfp8: MXFP4-weight workloads only); "
+                         "default: the workload's own")
     ap.add_argument("--weight-copies", type=int, default=4,
                     help="MXFP4 decode: copies of the weights the steps rotate over")
     ap.add_argument("--calib-copy", action="store_true",
@@ -72,7 +76,13 @@ def parse():
 # Oracle sample per workload (tokens, or rows of the pre-grouped layout):
 # about 2-8 s of float64 BLAS work on 16 host threads each.
 CPU_SAMPLE = {"fine_grained_prefill": 512, "mixtral_prefill": 1024, "mxfp4_decode": 32, "pregrouped": 1024,
-              "tiny": 64}
+              "tiny": 64, "mxfp4_prefill": 16}
+
+
+def is_decode(wl) -> bool:
+    """MXFP4 workloads with at most 32 routed rows per expert: the weight
+    stream is the metric (GB/s); everything else is a prefill (TFLOP/s)."""
+    return wl.wfmt == "mxfp4" and wl.T * wl.k <= 32 * wl.E
 
 
 def timed_passes(step, K, hev, n_ev, extra=None):
@@ -130,12 +140,14 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def kernel_source_hash(wfmt: str) -> str:
-    """sha256 of the sources the GEMM1 kernel of a weight format is built from
-    (bf16: the prefill GEMM; mxfp4: the decode GEMM)."""
+def kernel_source_hash(kind: str) -> str:
+    """sha256 of the sources a GEMM1 kernel is built from (bf16: the prefill
+    GEMM; mxfp4: the decode GEMM; mx_prefill: the block-scaled prefill GEMM)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("common.hpp", "gemm_bf16.hpp" if wfmt == "bf16" else "gemm_skinny.hpp"):
+    files = {"bf16": ("common.hpp", "gemm_bf16.hpp"), "mxfp4": ("common.hpp", "gemm_skinny.hpp"),
+             "mx_prefill": ("common.hpp", "gemm_bf16.hpp", "gemm_mx.hpp")}[kind]
+    for f in files:
         with open(os.path.join(ROOT, "mixture_experts_expert_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -208,7 +220,7 @@ def cpu_baseline(wl, x, ids, w, W, S, n_tokens, act_fmt="bf16"):
     oracle.experts_forward(xs, ids_c, w[:n_tokens], *Wh, **kw)
     dt = time.perf_counter() - t0
     slots = int(np.sum(ids_c >= 0))
-    if wl.wfmt == "mxfp4":
+    if is_decode(wl):
         value = len(touched) * 3 * wl.H * wl.I * (0.5 + 1 / 32) / dt / 1e9
         unit = "GB/s"
     else:
@@ -326,7 +338,7 @@ def run_token_major(args, wl, dev, K, act_fmt):
     if wl.wfmt == "mxfp4":
         (cg, sg), (cu, su), (cd, sd) = synth.make_mxfp4_weights(wl, device=dev)
         W, S = (cg, cu, cd), (sg, su, sd)
-        copies = max(1, args.weight_copies)
+        copies = max(1, args.weight_copies) if is_decode(wl) else 1
     else:
         W, S = synth.make_bf16_weights(wl, device=dev), (None, None, None)
         copies = 1
@@ -378,11 +390,23 @@ def run_token_major(args, wl, dev, K, act_fmt):
     M = wl.T * wl.k
     n_touched, wbytes = touched_weight_bytes(wl, ids)
     avg = {s: float(np.mean(v)) for s, v in stage_ms.items()}
-    single = bool(B.moe_experts_workspace_layout(p).single_launch)
+    lay = B.moe_experts_workspace_layout(p)
+    single = bool(lay.single_launch)
     if single:  # GEMM1, GEMM2 and the combine share one launch after the align
         avg = {"align": avg["align"], "gemm1+gemm2+combine": avg["gemm1"] + avg["gemm2"] + avg["combine"],
                **({"router": avg["router"]} if "router" in avg else {})}
-    if wl.wfmt == "bf16":
+    if lay.mx_tiled:  # the token rows' quantization and the scale blocks run before GEMM1
+        avg = {("align+quant+prep" if s == "align" else s): v for s, v in avg.items()}
+        unit = "TFLOP/s"
+        value = wl.flops / (ms_per_step * 1e-3) / 1e12
+        g1_flops = 4.0 * M * wl.H * wl.I
+        achieved = g1_flops / (avg["gemm1"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": counter_traffic(wl.name, "mx_prefill"),
+                "kernel": "gemm1 (gate+up, MXFP4 weights x MXFP8 activations, v_mfma_scale_f32_32x32x64_f8f6f4)",
+                "algorithmic_bytes": int(n_touched * 2 * wl.I * wl.H * (0.5 + 1 / 32) + wl.T * wl.H * (1 + 1 / 32)
+                                         + M * wl.I * (1 + 1 / 32))}
+    elif wl.wfmt == "bf16":
         unit = "TFLOP/s"
         value = wl.flops / (ms_per_step * 1e-3) / 1e12
         g1_flops = 4.0 * M * wl.H * wl.I
@@ -440,9 +464,9 @@ def run_one(args, name, dev, K):
     import torch
     import synth
     wl = synth.workload(name)
-    if wl.wfmt == "mxfp4":
+    if is_decode(wl):
         K = max(K, DECODE_MIN_STEPS)
-    act_fmt = args.act_fmt if wl.wfmt == "mxfp4" else "bf16"
+    act_fmt = (args.act_fmt or wl.act_fmt) if wl.wfmt == "mxfp4" else "bf16"
     res = run_pregrouped(args, wl, dev, K) if wl.pregrouped else run_token_major(args, wl, dev, K, act_fmt)
     gc.collect()
     torch.cuda.empty_cache()
@@ -453,7 +477,8 @@ def main():
     args = parse()
     if args.print_source_hash:
         import synth
-        print(kernel_source_hash(synth.WORKLOADS[args.workload].wfmt))
+        wl = synth.WORKLOADS[args.workload]
+        print(kernel_source_hash("mx_prefill" if wl.act_fmt == "mxfp8" and not is_decode(wl) else wl.wfmt))
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the experts step "
@@ -470,7 +495,7 @@ def main():
         if n not in synth.WORKLOADS:
             print(f"bench.py: unknown workload {n!r}", file=sys.stderr)
             sys.exit(2)
-    if args.act_fmt != "bf16" and all(synth.WORKLOADS[n].wfmt != "mxfp4" for n in names):
+    if args.act_fmt not in (None, "bf16") and all(synth.WORKLOADS[n].wfmt != "mxfp4" for n in names):
         print(f"bench.py: --act-fmt {args.act_fmt} needs an MXFP4-weight workload", file=sys.stderr)
         sys.exit(2)
     results = {}

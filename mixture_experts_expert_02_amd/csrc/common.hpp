@@ -48,14 +48,21 @@ struct ActParams {
   float alpha, beta, limit;
 };
 
-__device__ __forceinline__ float gated_act(const ActParams& a, float g, float u) {
-  if (a.kind == 0) return g * sigmoidf_fast(g) * u;
-  if (a.kind == 2)  // SiTu (trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsBase constructor comment)
+// AK >= 0: the kind fixed at compile time (the prefill GEMMs' epilogues, which
+// evaluate it for 64 values per lane, are instantiated per kind so that each
+// carries one formula's code); AK < 0: a.kind at run time.
+template <int AK>
+__device__ __forceinline__ float gated_act_k(const ActParams& a, float g, float u) {
+  const int kind = AK >= 0 ? AK : a.kind;
+  if (kind == 0) return g * sigmoidf_fast(g) * u;
+  if (kind == 2)  // SiTu (trtllm_mxfp4_moe page, TrtLlmMxfp4ExpertsBase constructor comment)
     return a.alpha * tanhf(g / a.alpha) * sigmoidf_fast(g) * (a.beta * tanhf(u / a.beta));
   g = fminf(g, a.limit);
   u = fminf(fmaxf(u, -a.limit), a.limit);
   return g * sigmoidf_fast(a.alpha * g) * (u + a.beta);
 }
+
+__device__ __forceinline__ float gated_act(const ActParams& a, float g, float u) { return gated_act_k<-1>(a, g, u); }
 
 // Per-expert parameters: device float32 arrays of one value per expert
 // (segment), or nullptr where the problem's scalar (or 1 for the scales)

@@ -113,9 +113,13 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 // operand reads) so that every lane stores 16 contiguous bytes: 128 rows x 32
 // columns per pass, rows padded to 40 elements against bank conflicts.
 // GEMM1 writes act = f(gate * es, up * es) * route weight; GEMM2 down * es.
+// GEMM1's route weights of the block's 128 rows go through the same LDS
+// region first (two loads per lane, one wait), so the activation math reads
+// four rows' weights with one LDS read instead of waiting on a global load
+// per group of rows.
 // wrows: rows of the block inside the segment; wrow0: first output row;
 // col0: first output column.
-template <bool GATED>
+template <bool GATED, int AK = 0>
 __device__ __forceinline__ void store_block_bf16(const f32x16 (&acc)[4][2], lds_u32x4* smem, int wave, int wrows,
                                                  int wrow0, int col0, int N, uint16_t* __restrict__ Cs,
                                                  const float* row_w, const ActParams& ap, float es) {
@@ -123,6 +127,16 @@ __device__ __forceinline__ void store_block_bf16(const f32x16 (&acc)[4][2], lds_
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lk = lane >> 5;
   lds_u16* sc = (lds_u16*)&smem[wave * 1024];
+  // row weights after the 128 x LDR staged values (10 KB of the wave's 16 KB)
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  typedef __attribute__((address_space(3))) float lds_float;
+  lds_float* wl = (lds_float*)(sc + 128 * LDR);
+  if (GATED) {
+    const float w0 = (row_w && lane < wrows) ? row_w[wrow0 + lane] : 1.f;
+    const float w1 = (row_w && 64 + lane < wrows) ? row_w[wrow0 + 64 + lane] : 1.f;
+    wl[lane] = w0;
+    wl[64 + lane] = w1;
+  }
   const int cc = lane & 3;  // 16-byte chunk of a staged 64-byte row
   const int rr = lane >> 2; // staged row within a group of 16
 #pragma unroll
@@ -132,17 +146,13 @@ __device__ __forceinline__ void store_block_bf16(const f32x16 (&acc)[4][2], lds_
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int rbase = i * 32 + rq * 8 + lk * 4;  // 4 consecutive rows r = rq*4 + 0..3
-        float w4[4] = {1.f, 1.f, 1.f, 1.f};
-        if (GATED) {
-#pragma unroll
-          for (int r3 = 0; r3 < 4; ++r3)
-            if (row_w && rbase + r3 < wrows) w4[r3] = row_w[wrow0 + rbase + r3];
-        }
+        f32x4 w4 = {1.f, 1.f, 1.f, 1.f};
+        if (GATED) w4 = *(const lds_f32x4*)&wl[rbase];
 #pragma unroll
         for (int r3 = 0; r3 < 4; ++r3) {
           const int r = rq * 4 + r3;
           float v;
-          if (GATED) v = gated_act(ap, acc[i][0][r] * es, acc[i][1][r] * es) * w4[r3];
+          if (GATED) v = gated_act_k<AK>(ap, acc[i][0][r] * es, acc[i][1][r] * es) * w4[r3];
           else v = acc[i][pass][r] * es;
           const __bf16 h = (__bf16)v;
           sc[(rbase + r3) * LDR + lr] = *(const uint16_t*)&h;
@@ -186,7 +196,7 @@ __device__ __forceinline__ void item_tile(const P& p, int item, int mtl, int nsp
   }
 }
 
-template <bool GATED>
+template <bool GATED, int AK>
 __device__ __forceinline__ void gemm_tile(const Params& p, int mt, int nt, int split, int nsplit,
                                           lds_u32x4* smem) {
   constexpr uint32_t STAGE_BYTES = 2 * STAGE_U4 * 16;
@@ -381,7 +391,7 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int mt, int nt, int s
 
   // ---- epilogue
   if (!active) return;
-  store_block_bf16<GATED>(acc, smem, wave, min(128, rows - wm * 128), row0 + wm * 128,
+  store_block_bf16<GATED, AK>(acc, smem, wave, min(128, rows - wm * 128), row0 + wm * 128,
                           n0 + (GATED ? wn * 32 : wn * 64), p.N, p.C + (size_t)split * p.c_split,
                           GATED ? p.row_w : nullptr, act_for(p.act, p.ep, seg),
                           scale_for(GATED ? p.ep.fc1 : p.ep.fc2, seg));  // fc1 on gate and up, fc2 on down
@@ -399,7 +409,7 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int mt, int nt, int s
 // of block 8 r + x, so each XCD's compute units run one block of tiles at a
 // time, in step, and tiles of a block read the same panels of A and B at the
 // same K at about the same time.
-template <bool GATED>
+template <bool GATED, int AK>
 __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   // NS stages of [A 32 KB | B 32 KB]
   __shared__ u32x4 smem_arr[NS * 2 * STAGE_U4];
@@ -416,7 +426,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
       if (item >= n_live) break;
       if (r) stage_barrier();  // every wave has read its staged results of the last tile
       item_tile(p, item, mtl, nsplit, mt, nt, split);
-      gemm_tile<GATED>(p, mt, nt, split, nsplit, smem);
+      gemm_tile<GATED, AK>(p, mt, nt, split, nsplit, smem);
     }
     return;
   }
@@ -429,7 +439,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   }
   if (item >= n_live) return;
   item_tile(p, item, mtl, nsplit, mt, nt, split);
-  gemm_tile<GATED>(p, mt, nt, split, nsplit, smem);
+  gemm_tile<GATED, AK>(p, mt, nt, split, nsplit, smem);
 }
 
 }  // namespace big

@@ -123,7 +123,7 @@ __device__ __forceinline__ void wait_lgkm(int n) {
   }
 }
 
-template <bool GATED>
+template <bool GATED, int AK>
 __device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int split, int nsplit, lds_u8* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -389,13 +389,14 @@ __device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int spl
   const ActParams ap = act_for(p.act, p.ep, seg);
   const float es = scale_for(GATED ? p.ep.fc1 : p.ep.fc2, seg);  // fc1 on gate and up, fc2 on down
   if constexpr (!GATED) {
-    big::store_block_bf16<false>(acc, (big::lds_u32x4*)smem, wave, wrows, wrow0, n0 + wn * 64, N,
+    big::store_block_bf16<false, 0>(acc, (big::lds_u32x4*)smem, wave, wrows, wrow0, n0 + wn * 64, N,
                                  p.C + (size_t)split * p.c_split, nullptr, ap, es);
   } else {
     // GEMM1: act = f(gate * es, up * es) * route weight, quantized as MXFP8
     // for GEMM2. The wave's 32 columns are one 32-value block of each row.
-    // Values go through the wave's 10 KB of LDS, 64 rows at a time (rows
-    // padded to 40 floats); then 4 lanes hold 8 columns each of a row, reduce
+    // f goes through the wave's 10 KB of LDS, 64 rows at a time (rows padded
+    // to 40 floats); then 4 lanes hold 8 columns each of a row, multiply by
+    // the row's route weight (loaded up front, one per lane and pass), reduce
     // the block's largest magnitude across the 4, and write 8 code bytes; the
     // first of them writes the scale byte into GEMM2's scale block.
     constexpr int LDR = 40;
@@ -404,6 +405,14 @@ __device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int spl
     const bool cols_ok = col < N;
     uint8_t* scb = p.Cq_sc + ((size_t)mt * p.n_tiles + nt) * SC_BYTES + sc_pos(wn);
     const int part = lane & 3;
+    float wrow[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        const int rw = 64 * h + pass * 16 + (lane >> 2);
+        wrow[h][pass] = (p.row_w && rw < wrows) ? p.row_w[wrow0 + rw] : 1.f;
+      }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -412,9 +421,7 @@ __device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int spl
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int rl = i2 * 32 + 8 * (r >> 2) + 4 * lq + (r & 3);  // row within the 64
-          const int rw = 64 * h + rl;                                // row within the wave's 128
-          const float w = (p.row_w && rw < wrows) ? p.row_w[wrow0 + rw] : 1.f;
-          sf[rl * LDR + lr] = gated_act(ap, acc[i][0][r] * es, acc[i][1][r] * es) * w;
+          sf[rl * LDR + lr] = gated_act_k<AK>(ap, acc[i][0][r] * es, acc[i][1][r] * es);
         }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
@@ -425,7 +432,7 @@ __device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int spl
         const int rw = 64 * h + rl;
         float v[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) v[c] = sf[rl * LDR + part * 8 + c];
+        for (int c = 0; c < 8; ++c) v[c] = sf[rl * LDR + part * 8 + c] * wrow[h][pass];
         float m = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(v[c]));
@@ -456,7 +463,7 @@ __device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int spl
 // One tile per workgroup, items numbered compactly over the live tiles (the
 // bf16 prefill kernel's order: groups of gn column tiles, row tiles inside a
 // group, K ranges fastest), each XCD taking a contiguous run of items.
-template <bool GATED>
+template <bool GATED, int AK>
 __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem_arr[NS * STAGE];
   lds_u8* smem = (lds_u8*)smem_arr;
@@ -471,7 +478,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   if (item >= n_live) return;
   int mt, nt, split;
   big::item_tile(p, item, mtl, nsplit, mt, nt, split);
-  mx_tile<GATED>(p, mt, nt, split, nsplit, smem);
+  mx_tile<GATED, AK>(p, mt, nt, split, nsplit, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -507,7 +514,16 @@ __device__ __forceinline__ uint32_t order_0213(uint32_t b0, uint32_t b1, uint32_
   return b0 | (b2 << 8) | (b1 << 16) | (b3 << 24);
 }
 
+// LDS bytes k_mx_prep needs: one panel's scale rows (256 rows x K/32 bytes)
+__host__ __device__ constexpr int prep_lds_bytes(int kmax) { return 256 * (kmax / 32); }
+
+// Weight panels: the panel's scale rows (contiguous in the [E, N, K/32]
+// layout: 128 gate + 128 up rows, or 256 down rows) are copied into LDS with
+// coalesced loads, then each stage's 1 KB block is written with coalesced
+// 4-byte stores (thread r = row r). Row tiles of GEMM1's activations: thread
+// r copies its row's scale bytes (one 4-byte load per stage).
 __global__ __launch_bounds__(256) void k_mx_prep(const PrepParams q) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t prep_lds[];
   const int r = threadIdx.x;
   int b = blockIdx.x;
   const int n1 = q.E * q.NT1, n2 = q.E * q.NT2;
@@ -518,14 +534,29 @@ __global__ __launch_bounds__(256) void k_mx_prep(const PrepParams q) {
     const int e = b / NTc, nt = b - e * NTc;
     if (q.counts[e] == 0) return;
     const int N = g1 ? q.I : q.H, KB = (g1 ? q.H : q.I) / 32;
-    const int n = min(g1 ? nt * 128 + (r & 127) : nt * 256 + r, N - 1);
-    const uint8_t* src = (g1 ? (r < 128 ? q.Sg : q.Su) : q.Sd) + ((size_t)e * N + n) * KB;
-    uint8_t* dst = (g1 ? q.WS1 : q.WS2) + ((size_t)(e * NTc + nt) * KT) * SC_BYTES + r * 4;
+    const int n0 = g1 ? nt * 128 : nt * 256;
+    const int per = g1 ? 128 : 256;               // rows of one source region
+    const int nrows = min(per, N - n0);           // rows of the panel inside N
+    for (int part = 0; part < (g1 ? 2 : 1); ++part) {
+      const uint8_t* src = (g1 ? (part ? q.Su : q.Sg) : q.Sd) + ((size_t)e * N + n0) * KB;
+      uint8_t* dst = prep_lds + part * 128 * KB;
+      const int nbytes = nrows * KB;
+      if ((((uintptr_t)src | (uintptr_t)nbytes) & 3u) == 0) {
+        for (int i = r; i < nbytes / 4; i += 256) ((uint32_t*)dst)[i] = ((const uint32_t*)src)[i];
+      } else {
+        for (int i = r; i < nbytes; i += 256) dst[i] = src[i];
+      }
+    }
+    __syncthreads();
+    // tile row r: rows past N repeat the panel's last row inside N
+    const int rr = g1 ? (r & 127) : r;
+    const uint8_t* row = prep_lds + ((g1 && r >= 128) ? 128 * KB : 0) + min(rr, nrows - 1) * KB;
+    uint8_t* out = (g1 ? q.WS1 : q.WS2) + ((size_t)(e * NTc + nt) * KT) * SC_BYTES + r * 4;
     for (int u = 0; u < KT; ++u) {
       uint32_t v[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) v[t] = 4 * u + t < KB ? src[4 * u + t] : 0u;
-      *(uint32_t*)(dst + (size_t)u * SC_BYTES) = order_0213(v[0], v[1], v[2], v[3]);
+      for (int t = 0; t < 4; ++t) v[t] = 4 * u + t < KB ? row[4 * u + t] : 0u;
+      *(uint32_t*)(out + (size_t)u * SC_BYTES) = order_0213(v[0], v[1], v[2], v[3]);
     }
     return;
   }

@@ -398,6 +398,9 @@ int set_attrs() {
   for (const void* f : fused)
     if (e == hipSuccess)
       e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, moe::skinny::scale_lds_bytes(4096));
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute((const void*)moe::mx::k_mx_prep, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            moe::mx::prep_lds_bytes(moe::skinny::kMaxMxfp4K));
   if (e != hipSuccess) return MOE_EHIP;
   g_attr_done = true;
   return MOE_OK;
@@ -509,7 +512,14 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     const int po = persistent_override();
     q.persistent = po < 0 ? 0 : po;
     if (q.persistent) nblk = std::max(8, q.ncu / 8 * 8);
-    hipLaunchKernelGGL((moe::big::k_gemm<GATED>), dim3((unsigned)nblk), dim3(moe::big::NT), 0, s, q);
+    const dim3 g((unsigned)nblk), b(moe::big::NT);
+    if constexpr (!GATED) {
+      hipLaunchKernelGGL((moe::big::k_gemm<false, 0>), g, b, 0, s, q);
+    } else {  // one instantiation per activation kind
+      if (p.act == MOE_ACT_SWIGLU_OAI) hipLaunchKernelGGL((moe::big::k_gemm<true, 1>), g, b, 0, s, q);
+      else if (p.act == MOE_ACT_SITU) hipLaunchKernelGGL((moe::big::k_gemm<true, 2>), g, b, 0, s, q);
+      else hipLaunchKernelGGL((moe::big::k_gemm<true, 0>), g, b, 0, s, q);
+    }
   }
   return launch_status();
 }
@@ -620,7 +630,9 @@ int forward_mx(const moe_problem& p, const Plan& pl, const void* x, const moe::A
   pp.SA1 = at<uint8_t>(ws, pl.sa1);
   const long long nprep = (long long)p.E * (pl.NT1 + pl.NT2) + pl.mt_cap;
   if (nprep > 0x7fffffffLL) return MOE_ENOTSUP;
-  hipLaunchKernelGGL(moe::mx::k_mx_prep, dim3((unsigned)nprep), dim3(256), 0, s, pp);
+  hipLaunchKernelGGL(moe::mx::k_mx_prep, dim3((unsigned)nprep), dim3(256),
+                     (size_t)moe::mx::prep_lds_bytes(std::max(p.H, p.I)), s, pp);
+  mark(1);
 
   int ncu = 0;
   int rc = device_cus(&ncu);
@@ -653,7 +665,12 @@ int forward_mx(const moe_problem& p, const Plan& pl, const void* x, const moe::A
   g.ep = expert_params(p);
   long long nblk = ((long long)pl.mt_cap * pl.NT1 + 7) / 8 * 8;
   if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
-  hipLaunchKernelGGL(moe::mx::k_gemm<true>, dim3((unsigned)nblk), dim3(moe::mx::NT), 0, s, g);
+  if (p.act == MOE_ACT_SWIGLU_OAI)
+    hipLaunchKernelGGL((moe::mx::k_gemm<true, 1>), dim3((unsigned)nblk), dim3(moe::mx::NT), 0, s, g);
+  else if (p.act == MOE_ACT_SITU)
+    hipLaunchKernelGGL((moe::mx::k_gemm<true, 2>), dim3((unsigned)nblk), dim3(moe::mx::NT), 0, s, g);
+  else
+    hipLaunchKernelGGL((moe::mx::k_gemm<true, 0>), dim3((unsigned)nblk), dim3(moe::mx::NT), 0, s, g);
   if ((rc = launch_status())) return rc;
   mark(2);
 
@@ -678,7 +695,7 @@ int forward_mx(const moe_problem& p, const Plan& pl, const void* x, const moe::A
   g2.row_w = nullptr;
   nblk = ((long long)pl.mt_cap * pl.NT2 * pl.s_cap + 7) / 8 * 8;
   if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
-  hipLaunchKernelGGL(moe::mx::k_gemm<false>, dim3((unsigned)nblk), dim3(moe::mx::NT), 0, s, g2);
+  hipLaunchKernelGGL((moe::mx::k_gemm<false, 0>), dim3((unsigned)nblk), dim3(moe::mx::NT), 0, s, g2);
   if ((rc = launch_status())) return rc;
   mark(3);
   moe::SplitSum ss{o.status, pl.NT2, pl.KT2, ncu, pl.s_cap, pl.M * p.H};
@@ -752,10 +769,7 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
     return rc;
   }
 
-  if (pl.mxbig) {
-    mark(1);
-    return forward_mx(*p, pl, x, o, wg, wu, wd, sg, su, sd, out, ws, s, mark);
-  }
+  if (pl.mxbig) return forward_mx(*p, pl, x, o, wg, wu, wd, sg, su, sd, out, ws, s, mark);
   GemmIO g1{x, o.perm, p->k, wg, wu, sg, su, p->I, p->H, at<void>(ws, pl.act), o.w_sorted, 1, 0, {}, {}};
   // MXFP8 activations: GEMM1's epilogue quantizes the activation rows for GEMM2 itself
   if (mx8) g1.Cq = quant_rows_at(ws, pl.aq, pl.M, p->I);

@@ -165,9 +165,11 @@ def mxfp8_activation_bounds(x, ids, w, W, S, act_kw, kernel_err_factor=1.0):
     return al, a_all, d_all, lambda e: oracle.expert_matrix(Wn[2], e)
 
 
-def mxfp8_extremes(a, d):
-    """The element values of smallest and largest magnitude within d of a."""
-    return np.sign(a) * np.maximum(np.abs(a) - d, 0.0), np.sign(a) * (np.abs(a) + d)
+def mxfp8_code_range(a, d):
+    """Smallest and largest e8m0 scale code per 32-block that values within d
+    of a can give (the code grows with the block's largest magnitude)."""
+    return (oracle.mxfp8_quantize(np.maximum(np.abs(a) - d, 0.0))[2].astype(np.int64),
+            oracle.mxfp8_quantize(np.abs(a) + d)[2].astype(np.int64))
 
 
 def mxfp8_reference_with_envelope(x, ids, w, W, S, act_kw, kernel_err_factor=1.0):
@@ -190,10 +192,10 @@ def mxfp8_reference_with_envelope(x, ids, w, W, S, act_kw, kernel_err_factor=1.0
     al, a, d, D_of = mxfp8_activation_bounds(x, ids, w, W, S, act_kw, kernel_err_factor)
     cu = al["cu_seqlens"]
     q, _, codes = oracle.mxfp8_quantize(a)
-    small, big = mxfp8_extremes(a, d)
+    c_lo, c_hi = mxfp8_code_range(a, d)
     dev = np.zeros_like(a)
-    for c in (codes, oracle.mxfp8_quantize(small)[2], oracle.mxfp8_quantize(big)[2]):
-        for v in (small, big):
+    for c in (codes, c_lo, c_hi):
+        for v in (a - d, a + d):  # rounding is monotone: the interval's ends bound its results
             dev = np.maximum(dev, np.abs(_quantize_with_codes(v, c) - q))
     M = T * k
     y = np.zeros((M, H))

@@ -13,7 +13,9 @@ import torch
 
 import oracle
 import synth
-from helpers import TOL, Guarded, LazyExperts, rel_err, to_np, wl_act_kw
+from helpers import (TOL, Guarded, LazyExperts, check_mxfp8_output, mxfp8_activation_bounds, mxfp8_code_range,
+                     mxfp8_reference_with_envelope, rel_err, to_np, wl_act_kw)
+from test_gpu_mxfp8 import check_split
 from mixture_experts_expert_02_amd import binding as B
 
 pytestmark = pytest.mark.gpu
@@ -107,3 +109,94 @@ def test_pregrouped_workload_full_tensor():
     print(f"[fullsize] pregrouped: all {wl.T} rows over {int(np.sum(lengths > 0))} non-empty segments "
           f"({row_tiles_covered(lengths, 256)} row tiles), max|err|/max|ref| {err:.2e}", flush=True)
     assert err <= TOL
+
+
+def test_mxfp4_prefill_workload_full_size():
+    """MXFP4 weights with MXFP8 activations at 8192 tokens (the LDS-tiled
+    block-scaled kernels). Every token: outputs written (NaN-poisoned
+    buffers), canary bands intact, run-to-run bit equality, the quantized
+    token rows bit for bit against the oracle's quantizer. The first 1024
+    tokens (4096 activation rows, every expert): each activation code and
+    scale GEMM1's epilogue wrote lies in the range the kernels' fp32 error
+    bound allows, and the outputs are within the tolerance beyond the
+    envelope of those decisions (helpers.mxfp8_reference_with_envelope; at
+    K = 2880 the worst-case bound leaves a wide envelope, so the plain error
+    is printed beside it)."""
+    wl = synth.workload("mxfp4_prefill")
+    print(f"[fullsize] mxfp4_prefill: T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.k} {wl.act} {wl.act_fmt}", flush=True)
+    x, ids, w, W, S = device_inputs(wl)
+    ids_d, w_d = torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
+    kw = wl_act_kw(wl)
+    p = B.problem(wl.T, wl.H, wl.I, wl.E, wl.k, wl.wfmt, **kw)
+    lay = B.moe_experts_workspace_layout(p)
+    assert lay.mx_tiled == 1 and lay.xq_rows == wl.T
+    ws = Guarded(B.moe_experts_workspace_bytes(p), DEV)
+    out = Guarded(wl.T * wl.H * 2, DEV)
+    outs = []
+    for rep in range(2):
+        ws.poison()
+        out.poison()
+        B.experts_forward(x, ids_d, w_d, *W, scales=S, out=out.view_bf16(wl.T, wl.H), workspace=ws.body, **kw)
+        torch.cuda.synchronize()
+        ws.check_bands()
+        out.check_bands()
+        outs.append(out.view_bf16(wl.T, wl.H).clone())
+    assert B.moe_device_error(ws.body) == 0
+    assert torch.equal(outs[0], outs[1]), "run-to-run results differ"
+    got = outs[0].float()
+    assert bool(torch.isfinite(got).all()), f"{int((~torch.isfinite(got)).sum())} output values not written"
+    check_split(ws.body, lay.xq, wl.T, wl.H, to_np(x), wl.T)
+
+    n = 1024
+    Wc, Sc = [t.cpu() for t in W], [t.cpu() for t in S]
+    kw8 = dict(kw)
+    sub = (x[:n].cpu(), ids[:n], w[:n], Wc, Sc, kw8)
+    # the sample's activation rows inside the full problem's sorted order
+    al_full = oracle.align(ids, wl.E)
+    al_sub, a64, d64, _ = mxfp8_activation_bounds(*sub)
+    full_rows = al_full["inv_perm"].reshape(wl.T, wl.k)[:n].reshape(-1)[al_sub["perm"]]
+    check_activation_codes(ws.body, lay, wl, al_full, full_rows, a64, d64)
+    ref, envl, n_amb = mxfp8_reference_with_envelope(*sub)
+    err, beyond, used = check_mxfp8_output(to_np(outs[0][:n]), ref, envl)
+    print(f"[fullsize] mxfp4_prefill: first {n} tokens max|err|/max|ref| {err:.2e}, beyond the decision envelope "
+          f"{beyond:.2e} ({used} outputs inside it, {n_amb} activation elements with an open decision)", flush=True)
+    assert beyond <= TOL
+
+
+def check_activation_codes(ws, lay, wl, al, rows, a64, d64):
+    """GEMM1's e4m3 activation codes and e8m0 scales (per-tile blocks) for
+    sorted rows `rows` of the full problem, against the oracle's values a64
+    and bounds d64 of those rows (in the same order)."""
+    I, M = wl.I, wl.T * wl.k
+    NTc = (I + 127) // 128
+    # tile and row-in-tile of every sorted row: 256-row tiles of each segment
+    cu = al["cu_seqlens"]
+    starts = np.concatenate([[0], cu[:-1]])
+    seg = np.searchsorted(cu, rows, side="right")
+    local = rows - starts[seg]
+    tiles_before = np.concatenate([[0], np.cumsum((np.diff(np.concatenate([[0], cu])) + 255) // 256)[:-1]])
+    tile = tiles_before[seg] + local // 256
+    in_tile = local % 256
+    blocks = ws[lay.aq_sc: lay.aq_sc + int(tile.max() + 1) * NTc * 1024].cpu().numpy()
+    KB = I // 32
+    sc = np.zeros((len(rows), KB), dtype=np.int64)
+    for cb in range(KB):
+        g, b = cb // 4, cb % 4
+        sc[:, cb] = blocks[(tile * NTc + g) * 1024 + in_tile * 4 + (((b & 1) << 1) | (b >> 1))]
+    codes = ws[lay.aq: lay.aq + M * I].view(M, I)[torch.as_tensor(rows, device=ws.device)]
+    got = codes.view(torch.float8_e4m3fn).to(torch.float64).cpu().numpy().reshape(len(rows), KB, 32)
+    c_lo, c_hi = mxfp8_code_range(a64, d64)
+    assert not ((sc < c_lo) | (sc > c_hi)).any(), "scale codes outside the range the kernels' precision allows"
+    X = np.ldexp(1.0, (sc - 127).astype(np.int32))[..., None]
+    lo = oracle.e4m3_round((a64 - d64).reshape(len(rows), KB, 32) / X)
+    hi = oracle.e4m3_round((a64 + d64).reshape(len(rows), KB, 32) / X)
+    far = (got < lo) | (got > hi)
+    if far.any():
+        detail = [f"row {int(rows[r])} (tile {int(tile[r])} row {int(in_tile[r])}) col {32 * b + i}: exact "
+                  f"{a64[r, 32 * b + i]!r} bound {d64[r, 32 * b + i]!r} scale code {int(sc[r, b])} gpu "
+                  f"{got[r, b, i]!r} allowed [{lo[r, b, i]!r}, {hi[r, b, i]!r}]" for r, b, i in np.argwhere(far)[:6]]
+        raise AssertionError(f"{int(far.sum())} activation codes outside their allowed range: {detail}")
+    _, elem, want = oracle.mxfp8_quantize(a64)
+    print(f"[fullsize] activation codes of {len(rows)} rows: {int((sc != want).sum())} scale codes and "
+          f"{int((got.reshape(elem.shape) != elem).sum())} elements differ from the oracle's own decisions, all "
+          f"within the kernels' fp32 error bound", flush=True)

@@ -23,7 +23,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import (TOL, check_mxfp8_output, mxfp8_activation_bounds, mxfp8_extremes,
+from helpers import (TOL, check_mxfp8_output, mxfp8_activation_bounds, mxfp8_code_range,
                      mxfp8_reference_with_envelope, rel_err, to_np)
 from mixture_experts_expert_02_amd import binding as B
 from test_gpu_forward import ACT_PARAMS, make_problem, oracle_out, run_gpu
@@ -130,9 +130,9 @@ def test_mx_prefill_quantized_rows(shape):
     activation rows GEMM1's epilogue writes (codes in sorted order, scales in
     the per-tile blocks) against the oracle's activation a and the bound d on
     the kernels' fp32 error (helpers.mxfp8_activation_bounds): each scale
-    code lies between the codes of the block taken at |a| - d and at |a| + d,
-    and each element, with the kernels' scale, between the e4m3 roundings of
-    a - d and a + d (rounding is monotone). Printed: how many codes and
+    code lies between the codes of the block taken at magnitudes |a| - d and
+    |a| + d, and each element, with the kernels' scale, between the e4m3
+    roundings of a - d and a + d (rounding is monotone). Printed: how many codes and
     elements differ from the oracle's own decisions."""
     T, H, I, E, k = shape
     print(f"[mx_prefill] quantized rows T={T} H={H} I={I} E={E} k={k}", flush=True)
@@ -172,16 +172,13 @@ def test_mx_prefill_quantized_rows(shape):
             t += 1
         start = end
     _, elem, want = oracle.mxfp8_quantize(a64)
-    small, big = mxfp8_extremes(a64, d64)
-    c_lo = oracle.mxfp8_quantize(small)[2].astype(np.int64)
-    c_hi = oracle.mxfp8_quantize(big)[2].astype(np.int64)
+    c_lo, c_hi = mxfp8_code_range(a64, d64)
     bad = (sc < c_lo) | (sc > c_hi)
     assert not bad.any(), f"{int(bad.sum())} scale codes outside the range the kernels' precision allows"
     X = np.ldexp(1.0, (sc - 127).astype(np.int32))[..., None]
     got = e4m3_bytes_to_f64(codes_ws).reshape(n_valid, I // 32, 32)
-    q_s = oracle.e4m3_round(small.reshape(n_valid, I // 32, 32) / X)
-    q_b = oracle.e4m3_round(big.reshape(n_valid, I // 32, 32) / X)
-    lo, hi = np.minimum(q_s, q_b), np.maximum(q_s, q_b)
+    lo = oracle.e4m3_round((a64 - d64).reshape(n_valid, I // 32, 32) / X)
+    hi = oracle.e4m3_round((a64 + d64).reshape(n_valid, I // 32, 32) / X)
     far = (got < lo) | (got > hi)
     if far.any():
         where = np.argwhere(far)[:6]

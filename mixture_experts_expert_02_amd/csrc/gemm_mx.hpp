@@ -41,6 +41,10 @@
 // call and GEMM1's activation blocks from the token rows' scales; GEMM1's
 // epilogue writes GEMM2's, since its column tile (128 activation columns) is
 // exactly one GEMM2 stage.
+//
+// Schedule: one workgroup per compute unit, each running a run of tiles with
+// the stage stream carried across tile boundaries (see mx_gemm); MFMAs of A
+// fragments whose 32 rows lie past the segment are skipped.
 #pragma once
 
 #include "common.hpp"
@@ -123,51 +127,218 @@ __device__ __forceinline__ void wait_lgkm(int n) {
   }
 }
 
+// One tile's load context for this lane: the tile's place in the problem and
+// the per-lane offsets of its loads (see mx_gemm).
+struct MxTile {
+  int mt, nt, split, seg, row0, rows, KT;
+  bool half;                 // the K range ends in a 64-K stage
+  uint32_t a_off[4], b_off[2];
+  const uint8_t* bbase;      // this wave's weight codes: the expert's gate / up / down rows
+  const uint8_t* sc_src;     // this wave's quarter of the scale blocks, first stage of the range
+};
+
+// Load assignment. A: wave w fills rows 32w..32w+31, 8 rows x 128 B per
+// instruction (lane l: row l / 8, slot l % 8). B: rows 32w..32w+31 of the B
+// half, 16 rows x 64 B per instruction (lane l: row l / 4, slot l % 4); in
+// GEMM1 waves 0-3 fill the gate rows, 4-7 the up rows. Scales: waves 0-3
+// copy a quarter of the stage's A block, 4-7 of its B block.
+template <bool GATED>
+__device__ __forceinline__ void mx_tile_ctx(const Params& p, int item, int mtl, int nsplit, int wave, int lane_in,
+                                            MxTile& t) {
+  int lane = lane_in;  // opaque: keeps the per-lane terms from being hoisted out of the tile loop
+  asm volatile("" : "+v"(lane));
+  big::item_tile(p, item, mtl, nsplit, t.mt, t.nt, t.split);
+  t.seg = p.tile_seg[t.mt];
+  t.row0 = p.tile_row0[t.mt];
+  t.rows = min(BM, p.seg_end[t.seg] - t.row0);
+  const int N = p.N, K = p.K;
+  const int n0 = t.nt * (GATED ? BN / 2 : BN);
+  const int st_lo = t.split * p.KT / nsplit;
+  t.KT = (t.split + 1) * p.KT / nsplit - st_lo;
+  t.half = (K % BK) != 0 && st_lo + t.KT == p.KT;
+  const uint32_t KB2 = (uint32_t)K / 2;
+  const int first = p.a_perm ? p.a_perm[t.row0] / p.a_div : t.row0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 32 + i * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    int arow = first;
+    if (r < t.rows) arow = p.a_perm ? p.a_perm[t.row0 + r] / p.a_div : t.row0 + r;
+    t.a_off[i] = r < t.rows ? (uint32_t)arow * (uint32_t)K + (uint32_t)(st_lo * BK + chunk * 16) : kNoLoad;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = wave * 32 + j * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((r >> 2) & 3);
+    const int n = n0 + (GATED ? (r & 127) : r);
+    t.b_off[j] = n < N ? (uint32_t)n * KB2 + (uint32_t)(st_lo * (BK / 2) + chunk * 16) : kNoLoad;
+  }
+  t.bbase = ((GATED && wave >= 4) ? p.B1 : p.B0) + (size_t)t.seg * N * KB2;
+  t.sc_src = wave < 4 ? p.A_sc + ((size_t)t.mt * p.KT + st_lo) * SC_BYTES + wave * 256
+                      : p.B_sc + (((size_t)t.seg * p.n_tiles + t.nt) * p.KT + st_lo) * SC_BYTES + (wave - 4) * 256;
+}
+
+// Epilogue of one tile. Each wave stages its 128 x 64 results (GEMM1: 128
+// rows x 32 activation columns) through its own 6400 bytes of one stage
+// buffer, 32 rows (one A fragment) at a time.
+//  * GEMM2: bf16 of acc * es, rows padded to 72 values; then 8 lanes write a
+//    row's 128 bytes, 8 rows per instruction.
+//  * GEMM1: act = f(gate * es, up * es) * route weight, quantized as MXFP8
+//    for GEMM2 (the wave's 32 columns are one 32-value block of each row).
+//    f goes through LDS as fp32, rows padded to 40 floats; then 4 lanes hold
+//    8 columns each of a row, reduce the block's largest magnitude across
+//    the 4, and write 8 code bytes; the first of them writes the scale byte
+//    into GEMM2's scale block.
+constexpr int EP_WAVE = STAGE / 8;  // staging bytes per wave
 template <bool GATED, int AK>
-__device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int split, int nsplit, lds_u8* smem) {
+__device__ __forceinline__ void mx_epilogue(const Params& p, const MxTile& t, const f32x16 (&acc)[4][2],
+                                            lds_u8* ebuf, int wave, int lane_in, int nfr) {
+  // an opaque copy of the lane index: the per-lane addresses below are then
+  // computed here, not hoisted out of the tile loop into registers that
+  // would be live through every K loop
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lr = lane & 31, lq = lane >> 5;
+  const int N = p.N;
+  const int n0 = t.nt * (GATED ? BN / 2 : BN);
+  const int wrows = min(128, t.rows - wm * 128);
+  const int wrow0 = t.row0 + wm * 128;
+  const ActParams ap = act_for(p.act, p.ep, t.seg);
+  const float es = scale_for(GATED ? p.ep.fc1 : p.ep.fc2, t.seg);  // fc1 on gate and up, fc2 on down
+  if constexpr (!GATED) {
+    static_assert(32 * 72 * 2 <= EP_WAVE, "GEMM2 staging");
+    constexpr int LDR = 72;
+    typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+    lds_u16_t* sh = (lds_u16_t*)(ebuf + wave * EP_WAVE);
+    uint16_t* Cs = p.C + (size_t)t.split * p.c_split;
+    const int col0 = n0 + wn * 64;
+    const int cc = lane & 7, rr = lane >> 3;
+    const bool col_ok = col0 + cc * 8 < N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= nfr) break;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = 8 * (r >> 2) + 4 * lq + (r & 3);
+          const __bf16 h = (__bf16)(acc[i][j][r] * es);
+          sh[rl * LDR + j * 32 + lr] = *(const uint16_t*)&h;
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const int rl = t4 * 8 + rr;
+        const u32x4 v = *(const lds_u32x4_t*)&sh[rl * LDR + cc * 8];
+        const int row = 32 * i + rl;
+        if (col_ok && row < wrows) *(u32x4*)(Cs + (size_t)(wrow0 + row) * N + col0 + cc * 8) = v;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  } else {
+    static_assert(32 * 40 * 4 <= EP_WAVE, "GEMM1 staging");
+    constexpr int LDR = 40;
+    lds_f32* sf = (lds_f32*)(ebuf + wave * EP_WAVE);
+    const int col = n0 + wn * 32;  // first activation column of the block
+    const bool cols_ok = col < N;
+    uint8_t* scb = p.Cq_sc + ((size_t)t.mt * p.n_tiles + t.nt) * SC_BYTES + sc_pos(wn);
+    const int part = lane & 3;
+    // route weights of the lane's 8 rows (rows past the tile read the last
+    // row's; their results are not stored)
+    float wrow[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) wrow[i][pass] = 1.f;
+    if (p.row_w) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass)
+          wrow[i][pass] = p.row_w[wrow0 + min(32 * i + pass * 16 + (lane >> 2), wrows - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= nfr) break;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = 8 * (r >> 2) + 4 * lq + (r & 3);
+        sf[rl * LDR + lr] = gated_act_k<AK>(ap, acc[i][0][r] * es, acc[i][1][r] * es);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int rl = pass * 16 + (lane >> 2);
+        const int rw = 32 * i + rl;
+        float v[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] = sf[rl * LDR + part * 8 + c] * wrow[i][pass];
+        float m = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(v[c]));
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        const int code = mx8_code(m);
+        const float inv = __uint_as_float((uint32_t)(254 - code) << 23);  // 2^(127 - code)
+        uint32_t w2[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          int h4 = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(v[4 * c2] * inv), sat448(v[4 * c2 + 1] * inv), 0, false);
+          h4 = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(v[4 * c2 + 2] * inv), sat448(v[4 * c2 + 3] * inv), h4, true);
+          w2[c2] = (uint32_t)h4;
+        }
+        if (rw < wrows) {
+          if (cols_ok) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            *(u32x2*)(p.Cq + (size_t)(wrow0 + rw) * N + col + part * 8) = u32x2{w2[0], w2[1]};
+          }
+          if (part == 0) scb[(size_t)(wm * 128 + rw) * 4] = cols_ok ? (uint8_t)code : (uint8_t)0;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
+// Tiles of a launch, one or more per workgroup. Items are numbered as in the
+// bf16 prefill kernel (groups of gn column tiles, row tiles inside a group, K
+// ranges fastest); XCD x (the hardware sends workgroup b to XCD b mod 8) owns
+// the contiguous run [x per, (x + 1) per) of them, and its S = gridDim / 8
+// workgroups take every S-th item of the run, so the tiles an XCD works on at
+// any time are neighbours. With a grid of all items each workgroup runs one
+// tile; with one workgroup per compute unit each runs its share in turn, and
+// the stage stream runs on across tiles: the two loads past a tile's last
+// stage fetch the next tile's first two stages, and the last stage's reads of
+// "the next stage" are the next tile's first operand reads, so a tile starts
+// without waiting for its loads. Its epilogue stages through the buffer of
+// the previous tile's last stage, the one buffer no load targets then.
+template <bool GATED, int AK>
+__device__ __forceinline__ void mx_gemm(const Params& p, lds_u8* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int N = p.N;
 
-  const int seg = p.tile_seg[mt];
-  const int row0 = p.tile_row0[mt];
-  const int rows = min(BM, p.seg_end[seg] - row0);
-  const int N = p.N, K = p.K;
-  const int n0 = nt * (GATED ? BN / 2 : BN);
-  const int st_lo = split * p.KT / nsplit;
-  const int KT = (split + 1) * p.KT / nsplit - st_lo;
-  const bool half = (K % BK) != 0 && st_lo + KT == p.KT;  // the range's last stage holds 64 K
+  const int mtl = p.status[2];
+  int nsplit = 1;
+  if (!GATED && p.s_cap > 1) nsplit = split_k_count(mtl * p.n_tiles, p.KT, p.ncu, p.s_cap);
+  const int n_live = mtl * p.n_tiles * nsplit;
+  const int per = (n_live + 7) >> 3;
+  const int x = blockIdx.x & 7, S = gridDim.x >> 3;
+  const int lo = x * per, hi = min(lo + per, n_live);
+  int item = lo + (int)(blockIdx.x >> 3);
+  if (item >= hi) return;
 
-  // ---- load assignment. A: wave w fills rows 32w..32w+31, 8 rows x 128 B
-  // per instruction (lane l: row l / 8, slot l % 8). B: rows 32w..32w+31 of
-  // the B half, 16 rows x 64 B per instruction (lane l: row l / 4, slot
-  // l % 4); in GEMM1 waves 0-3 fill the gate rows, 4-7 the up rows. Scales:
-  // waves 0-3 copy a quarter of the stage's A block, 4-7 of its B block.
-  const uint32_t KB2 = (uint32_t)K / 2;
-  uint32_t a_off[4], b_off[2];
-  {
-    const int first = p.a_perm ? p.a_perm[row0] / p.a_div : row0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wave * 32 + i * 8 + (lane >> 3);
-      const int chunk = (lane & 7) ^ ((r >> 1) & 7);
-      int arow = first;
-      if (r < rows) arow = p.a_perm ? p.a_perm[row0 + r] / p.a_div : row0 + r;
-      a_off[i] = r < rows ? (uint32_t)arow * (uint32_t)K + (uint32_t)(st_lo * BK + chunk * 16) : kNoLoad;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = wave * 32 + j * 16 + (lane >> 2);
-      const int chunk = (lane & 3) ^ ((r >> 2) & 3);
-      const int n = n0 + (GATED ? (r & 127) : r);
-      b_off[j] = n < N ? (uint32_t)n * KB2 + (uint32_t)(st_lo * (BK / 2) + chunk * 16) : kNoLoad;
-    }
-  }
   const __amdgpu_buffer_rsrc_t rsA = operand_rsrc(p.A, p.a_bytes);
-  const uint8_t* Bw = (GATED && wave >= 4) ? p.B1 : p.B0;
-  const __amdgpu_buffer_rsrc_t rsB = operand_rsrc(Bw + (size_t)seg * N * KB2, (uint32_t)N * KB2);
-  const uint8_t* sc_src = wave < 4 ? p.A_sc + ((size_t)mt * p.KT + st_lo) * SC_BYTES + wave * 256
-                                   : p.B_sc + (((size_t)seg * p.n_tiles + nt) * p.KT + st_lo) * SC_BYTES + (wave - 4) * 256;
+  const uint32_t wbytes = (uint32_t)N * ((uint32_t)p.K / 2);
+  MxTile cur, nxt;
+  mx_tile_ctx<GATED>(p, item, mtl, nsplit, wave, lane, cur);
+  bool has_next = item + S < hi;
+  mx_tile_ctx<GATED>(p, has_next ? item + S : item, mtl, nsplit, wave, lane, nxt);
 
   // A chunks of the high half of a stage (K 64..127 of it) for this lane's
   // rows: the swizzle makes chunk bit 2 = lane bit 2 for even load
@@ -177,31 +348,35 @@ __device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int spl
   const uint32_t hi_even = (lane & 4) ? kNoLoad : 0u;
   const uint32_t hi_odd = (lane & 4) ? 0u : kNoLoad;
 
-  // One load instruction of stage u (local index) into buffer b: q = 0..3 A,
-  // 4, 5 B, 6 the scale quarter (lanes 0-15). Every wave issues all seven in
-  // every stage; for u >= KT the codes' offsets are past the end (nothing is
-  // read) and the scale copy repeats the last stage's block.
-#define MOE_MX_DMA(b, u, q)                                                                                    \
+  // One load instruction of stage U of the stream (U < cur.KT: the current
+  // tile's stage U; else the next tile's stage U - cur.KT) into buffer b:
+  // q = 0..3 A, 4, 5 B, 6 the scale quarter (lanes 0-15). Every wave issues
+  // all seven for every stage; a stage that does not exist reads nothing
+  // (offsets past the end) and the scale copy repeats a block of the tile.
+#define MOE_MX_DMA(b, U, q)                                                                                    \
   {                                                                                                            \
+    const bool in_cur = (U) < cur.KT;                                                                          \
+    const int u = in_cur ? (U) : (U) - cur.KT;                                                                 \
+    const int ktx = in_cur ? cur.KT : nxt.KT;                                                                  \
+    const uint32_t kill = (in_cur || (has_next && u < nxt.KT)) ? 0u : kNoLoad;                                 \
     lds_u8* dst = smem + (b) * STAGE;                                                                          \
-    const uint32_t kill = (u) < KT ? 0u : kNoLoad;                                                             \
     if ((q) < 4) {                                                                                             \
-      uint32_t off = (a_off[(q) & 3] + (uint32_t)(u) * BK) | kill;                                             \
-      if (half && (u) == KT - 1) off |= ((q) & 1) ? hi_odd : hi_even;                                          \
+      uint32_t off = ((in_cur ? cur.a_off[(q) & 3] : nxt.a_off[(q) & 3]) + (uint32_t)u * BK) | kill;           \
+      if ((in_cur ? cur.half : nxt.half) && u == ktx - 1) off |= ((q) & 1) ? hi_odd : hi_even;                 \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (__attribute__((address_space(3))) void*)(dst + (wave * 32 + (q) * 8) * 128), \
                                                16, off, 0, 0, 0);                                              \
     } else if ((q) < 6) {                                                                                      \
+      const __amdgpu_buffer_rsrc_t rsB = operand_rsrc(in_cur ? cur.bbase : nxt.bbase, wbytes);                 \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (__attribute__((address_space(3))) void*)(dst + A_BYTES + (wave * 32 + ((q) - 4) * 16) * 64), \
-                                               16, (b_off[(q) & 1] + (uint32_t)(u) * (BK / 2)) | kill, 0, 0, 0); \
+                                               16, ((in_cur ? cur.b_off[(q) & 1] : nxt.b_off[(q) & 1]) + (uint32_t)u * (BK / 2)) | kill, 0, 0, 0); \
     } else if (lane < 16) {                                                                                    \
-      __builtin_amdgcn_global_load_lds(sc_src + (size_t)min((int)(u), KT - 1) * SC_BYTES + lane * 16,          \
+      __builtin_amdgcn_global_load_lds((in_cur ? cur.sc_src : nxt.sc_src) + (size_t)min(u, ktx - 1) * SC_BYTES + lane * 16, \
                                        (__attribute__((address_space(3))) void*)(dst + A_BYTES + B_BYTES + wave * 256), 16, 0, 0); \
     }                                                                                                          \
   }
 
   // ---- wave tile: 128 rows x 64 weight rows (GEMM1: 32 gate + the same 32 up)
   const int wm = wave >> 2, wn = wave & 3;
-  const bool active = rows > wm * 128;
   const int lr = lane & 31, lq = lane >> 5;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   // per-lane LDS byte addresses inside a stage: A fragment 0 of step s (two
@@ -224,13 +399,6 @@ __device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int spl
       lds0 + (uint32_t)(A_BYTES + B_BYTES + SC_BYTES + (GATED ? wn * 32 + lr : wn * 64 + lr) * 4 + 2 * lq);
 
   f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
   // Operands: A fragment k = (lo, hi) 16-byte halves, one set (each
   // fragment is re-read for the next step right after the MFMA pair that
   // used it); B fragments of step 0 (fb) and step 1 (gb); scale pairs of the
@@ -283,9 +451,13 @@ __device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int spl
     wait_lgkm(n);                                                              \
     asm volatile("" : "+v"(fal[k]), "+v"(fah[k]));                             \
   }
-  // MFMA pair of A fragment k in step S with B fragments bb
+  // MFMA pair of A fragment k in step S with B fragments bb, skipped when
+  // the fragment's 32 rows are all past the segment (nfr = the wave's
+  // fragments holding rows). The empty asm reading the two accumulators
+  // keeps instruction selection from sinking the pair (which depends on
+  // nothing after it) below the next reads.
 #define MOE_MX_MFMA2(bb, k, S)                                                                               \
-  if (ACT_) {                                                                                                \
+  if ((k) < nfr) {                                                                                           \
     const i32x8 av = __builtin_shufflevector(fal[k], fah[k], 0, 1, 2, 3, 4, 5, 6, 7);                        \
     const i32x8 b0v = __builtin_shufflevector(bb[0], bb[0], 0, 1, 2, 3, -1, -1, -1, -1);                      \
     const i32x8 b1v = __builtin_shufflevector(bb[1], bb[1], 0, 1, 2, 3, -1, -1, -1, -1);                      \
@@ -294,33 +466,41 @@ __device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int spl
     asm volatile("" : "+v"(acc[k][0]), "+v"(acc[k][1]));                                                     \
   }
 
-  // ---- prologue: stages 0 and 1 in flight, wait for stage 0
+  // the operands of step 0 of the stage in buffer b (issue order A0, B,
+  // scales, A1, A2, A3: the order the loop's waits count on)
+#define MOE_MX_FIRST_READS(b)                                                  \
+  {                                                                            \
+    const uint32_t fbase = (uint32_t)(b) * STAGE;                              \
+    MOE_MX_READ_A(0, 0, fbase)                                                 \
+    MOE_MX_READ_B(fb, 0, fbase)                                                \
+    MOE_MX_READ_SC(fbase)                                                      \
+    MOE_MX_READ_A(0, 1, fbase)                                                 \
+    MOE_MX_READ_A(0, 2, fbase)                                                 \
+    MOE_MX_READ_A(0, 3, fbase)                                                 \
+  }
+
+  // ---- the first tile's stages 0 and 1 (or the next tile's first stage)
+  int base = 0;  // buffer of the current tile's stage 0
 #pragma unroll
   for (int q = 0; q < LOADS; ++q) MOE_MX_DMA(0, 0, q)
 #pragma unroll
   for (int q = 0; q < LOADS; ++q) MOE_MX_DMA(1, 1, q)
   big::wait_vmcnt<LOADS>();
   big::stage_barrier();
-  MOE_MX_READ_A(0, 0, 0u)
-  MOE_MX_READ_B(fb, 0, 0u)
-  MOE_MX_READ_SC(0u)
-  MOE_MX_READ_A(0, 1, 0u)
-  MOE_MX_READ_A(0, 2, 0u)
-  MOE_MX_READ_A(0, 3, 0u)
+  MOE_MX_FIRST_READS(0)
 
   // Stage s in buffer st. Step 0 runs on fb and the A fragments, with the
-  // loads of stage s + 2 (into buffer st2, free since the last barrier) and
-  // the reads of step 1's operands; step 1 runs on gb: after its first MFMA
-  // pair a wave waits for its loads of stage s + 1 and meets the others, and
-  // the reads of stage s + 1's step-0 operands and scales follow. The body
-  // is the same for every stage: past the last stage the loads read nothing
-  // and the reads fetch unused values from a stage buffer, so the wait
-  // counts never change.
+  // loads of stream stage s + 2 (into buffer st2, free since the last
+  // barrier) and the reads of step 1's operands; step 1 runs on gb: after its
+  // first MFMA pair a wave waits for its loads of stage s + 1 and meets the
+  // others, and the reads of stage s + 1's step-0 operands and scales follow
+  // (at the tile's last stage: the next tile's first operands). The body is
+  // the same for every stage, so the wait counts never change.
 #define MOE_MX_KLOOP                                                              \
   {                                                                               \
-    int st = 0, st1 = 1, st2 = 2;                                                 \
-    for (int s = 0; s < KT; ++s) {                                                \
-      const uint32_t base = (uint32_t)st * STAGE;                                 \
+    int st = base, st1 = base == NS - 1 ? 0 : base + 1, st2 = st1 == NS - 1 ? 0 : st1 + 1; \
+    for (int s = 0; s < cur.KT; ++s) {                                            \
+      const uint32_t sbase = (uint32_t)st * STAGE;                                \
       const uint32_t nbase = (uint32_t)st1 * STAGE;                               \
       _Pragma("unroll") for (int k = 0; k < 4; ++k) {                             \
         if (k == 0) {                                                             \
@@ -336,8 +516,8 @@ __device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int spl
         MOE_MX_MFMA2(fb, k, 0)                                                    \
         MOE_MX_DMA(st2, s + 2, 2 * k)                                             \
         if (k < 3) MOE_MX_DMA(st2, s + 2, 2 * k + 1)                              \
-        MOE_MX_READ_A(1, k, base)                                                 \
-        if (k == 0) MOE_MX_READ_B(gb, 1, base)                                    \
+        MOE_MX_READ_A(1, k, sbase)                                                \
+        if (k == 0) MOE_MX_READ_B(gb, 1, sbase)                                   \
       }                                                                           \
       _Pragma("unroll") for (int k = 0; k < 4; ++k) {                             \
         if (k == 0) {                                                             \
@@ -362,13 +542,42 @@ __device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int spl
       st2 = (st2 == NS - 1) ? 0 : st2 + 1;                                        \
     }                                                                             \
   }
-  if (active) {
-    constexpr bool ACT_ = true;
+
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    // A fragments of this wave with rows in the segment (a partial tile's
+    // MFMAs are skipped 32 rows at a time)
+    const int nfr = min(4, max(0, (cur.rows - wm * 128 + 31) >> 5));
     MOE_MX_KLOOP
-  } else {
-    constexpr bool ACT_ = false;
-    MOE_MX_KLOOP
+    // Every wave's operand reads of this tile are done once its own are: the
+    // buffer of the last stage is free for the epilogue's staging (the
+    // loads in flight target the other two). The last stage's reads of the
+    // next tile's first operands are dropped (their registers would be live
+    // through the epilogue) and made again after it.
+    // After the last tile only the loads past its end (which read nothing)
+    // are in flight; they land before the epilogue, so no load into LDS
+    // outlives the workgroup.
+    if (!has_next) big::wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    big::stage_barrier();
+    lds_u8* ebuf = smem + ((base + cur.KT - 1) % NS) * STAGE;
+    if (nfr > 0) mx_epilogue<GATED, AK>(p, cur, acc, ebuf, wave, lane, nfr);
+    if (!has_next) break;
+    // the epilogue's buffer takes the next tile's third stage
+    big::stage_barrier();
+    item += S;
+    base = (base + cur.KT) % NS;
+    cur = nxt;
+    has_next = item + S < hi;
+    mx_tile_ctx<GATED>(p, has_next ? item + S : item, mtl, nsplit, wave, lane, nxt);
+    MOE_MX_FIRST_READS(base)
   }
+#undef MOE_MX_FIRST_READS
 #undef MOE_MX_KLOOP
 #undef MOE_MX_MFMA2
 #undef MOE_MX_WAIT
@@ -378,107 +587,12 @@ __device__ __forceinline__ void mx_tile(const Params& p, int mt, int nt, int spl
 #undef MOE_DSR16
 #undef MOE_DSR
 #undef MOE_MX_DMA
-  // every wave has finished its LDS reads: the stage buffers are free for the
-  // epilogue's staging
-  big::wait_vmcnt<0>();
-  big::stage_barrier();
-  if (!active) return;
-
-  const int wrows = min(128, rows - wm * 128);
-  const int wrow0 = row0 + wm * 128;
-  const ActParams ap = act_for(p.act, p.ep, seg);
-  const float es = scale_for(GATED ? p.ep.fc1 : p.ep.fc2, seg);  // fc1 on gate and up, fc2 on down
-  if constexpr (!GATED) {
-    big::store_block_bf16<false, 0>(acc, (big::lds_u32x4*)smem, wave, wrows, wrow0, n0 + wn * 64, N,
-                                 p.C + (size_t)split * p.c_split, nullptr, ap, es);
-  } else {
-    // GEMM1: act = f(gate * es, up * es) * route weight, quantized as MXFP8
-    // for GEMM2. The wave's 32 columns are one 32-value block of each row.
-    // f goes through the wave's 10 KB of LDS, 64 rows at a time (rows padded
-    // to 40 floats); then 4 lanes hold 8 columns each of a row, multiply by
-    // the row's route weight (loaded up front, one per lane and pass), reduce
-    // the block's largest magnitude across the 4, and write 8 code bytes; the
-    // first of them writes the scale byte into GEMM2's scale block.
-    constexpr int LDR = 40;
-    lds_f32* sf = (lds_f32*)(smem + wave * 64 * LDR * 4);
-    const int col = n0 + wn * 32;  // first activation column of the block
-    const bool cols_ok = col < N;
-    uint8_t* scb = p.Cq_sc + ((size_t)mt * p.n_tiles + nt) * SC_BYTES + sc_pos(wn);
-    const int part = lane & 3;
-    float wrow[2][4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int pass = 0; pass < 4; ++pass) {
-        const int rw = 64 * h + pass * 16 + (lane >> 2);
-        wrow[h][pass] = (p.row_w && rw < wrows) ? p.row_w[wrow0 + rw] : 1.f;
-      }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i2 = 0; i2 < 2; ++i2) {
-        const int i = 2 * h + i2;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = i2 * 32 + 8 * (r >> 2) + 4 * lq + (r & 3);  // row within the 64
-          sf[rl * LDR + lr] = gated_act_k<AK>(ap, acc[i][0][r] * es, acc[i][1][r] * es);
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int pass = 0; pass < 4; ++pass) {
-        const int rl = pass * 16 + (lane >> 2);
-        const int rw = 64 * h + rl;
-        float v[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) v[c] = sf[rl * LDR + part * 8 + c] * wrow[h][pass];
-        float m = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(v[c]));
-        m = fmaxf(m, __shfl_xor(m, 1));
-        m = fmaxf(m, __shfl_xor(m, 2));
-        const int code = mx8_code(m);
-        const float inv = __uint_as_float((uint32_t)(254 - code) << 23);  // 2^(127 - code)
-        uint32_t w2[2];
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          int h4 = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(v[4 * c2] * inv), sat448(v[4 * c2 + 1] * inv), 0, false);
-          h4 = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(v[4 * c2 + 2] * inv), sat448(v[4 * c2 + 3] * inv), h4, true);
-          w2[c2] = (uint32_t)h4;
-        }
-        if (rw < wrows) {
-          if (cols_ok) {
-            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-            *(u32x2*)(p.Cq + (size_t)(wrow0 + rw) * N + col + part * 8) = u32x2{w2[0], w2[1]};
-          }
-          if (part == 0) scb[(size_t)(wm * 128 + rw) * 4] = cols_ok ? (uint8_t)code : (uint8_t)0;
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
 }
 
-// One tile per workgroup, items numbered compactly over the live tiles (the
-// bf16 prefill kernel's order: groups of gn column tiles, row tiles inside a
-// group, K ranges fastest), each XCD taking a contiguous run of items.
 template <bool GATED, int AK>
 __global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem_arr[NS * STAGE];
-  lds_u8* smem = (lds_u8*)smem_arr;
-  const int mtl = p.status[2];
-  int nsplit = 1;
-  if (!GATED && p.s_cap > 1) nsplit = split_k_count(mtl * p.n_tiles, p.KT, p.ncu, p.s_cap);
-  const int n_live = mtl * p.n_tiles * nsplit;
-  const int per = (n_live + 7) >> 3;
-  const int j = blockIdx.x >> 3;
-  if (j >= per) return;
-  const int item = (blockIdx.x & 7) * per + j;
-  if (item >= n_live) return;
-  int mt, nt, split;
-  big::item_tile(p, item, mtl, nsplit, mt, nt, split);
-  mx_tile<GATED, AK>(p, mt, nt, split, nsplit, smem);
+  mx_gemm<GATED, AK>(p, (lds_u8*)smem_arr);
 }
 
 // ---------------------------------------------------------------------------

@@ -663,7 +663,13 @@ int forward_mx(const moe_problem& p, const Plan& pl, const void* x, const moe::A
   g.row_w = p.weight_on_input ? nullptr : o.w_sorted;
   g.act = act_params(p);
   g.ep = expert_params(p);
+  // Persistent (the default): one workgroup per compute unit (a tile's
+  // 150 KB of LDS leaves room for no second one), each running its XCD's
+  // tiles in turn, the next tile's first loads under the current epilogue.
+  const bool mx_persist = persistent_override() != 0;
+  const long long pgrid = std::max(8, ncu / 8 * 8);
   long long nblk = ((long long)pl.mt_cap * pl.NT1 + 7) / 8 * 8;
+  if (mx_persist) nblk = std::min(nblk, pgrid);
   if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
   if (p.act == MOE_ACT_SWIGLU_OAI)
     hipLaunchKernelGGL((moe::mx::k_gemm<true, 1>), dim3((unsigned)nblk), dim3(moe::mx::NT), 0, s, g);
@@ -694,6 +700,7 @@ int forward_mx(const moe_problem& p, const Plan& pl, const void* x, const moe::A
   g2.Cq_sc = nullptr;
   g2.row_w = nullptr;
   nblk = ((long long)pl.mt_cap * pl.NT2 * pl.s_cap + 7) / 8 * 8;
+  if (mx_persist) nblk = std::min(nblk, pgrid);
   if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
   hipLaunchKernelGGL((moe::mx::k_gemm<false, 0>), dim3((unsigned)nblk), dim3(moe::mx::NT), 0, s, g2);
   if ((rc = launch_status())) return rc;

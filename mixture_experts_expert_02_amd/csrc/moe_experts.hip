@@ -356,9 +356,9 @@ int group_cols_override() {
   return v;
 }
 
-// Tuning override for the prefill GEMM's schedule: MOE_EXPERTS_PERSISTENT=1
-// (one workgroup per compute unit, lockstep rounds) or 0 (one workgroup per
-// tile); read once; unset = built-in choice.
+// Tuning override for the MXFP4 x MXFP8 prefill GEMMs' schedule:
+// MOE_EXPERTS_PERSISTENT=0 runs one workgroup per tile instead of one per
+// compute unit; read once.
 int persistent_override() {
   static const int v = [] {
     const char* e = std::getenv("MOE_EXPERTS_PERSISTENT");
@@ -501,7 +501,6 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     q.act = act_params(p);
     q.ep = expert_params(p);
     q.gn = std::min(q.n_tiles, group_cols_override() ? group_cols_override() : 2);
-    q.xcd_remap = 1;
     q.s_cap = GATED ? 1 : io.s_cap;
     q.c_split = io.c_split;
     int rc = device_cus(&q.ncu);
@@ -509,9 +508,6 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     long long nblk = (long long)pl.mt_cap * q.n_tiles * q.s_cap;
     nblk = (nblk + 7) / 8 * 8;
     if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
-    const int po = persistent_override();
-    q.persistent = po < 0 ? 0 : po;
-    if (q.persistent) nblk = std::max(8, q.ncu / 8 * 8);
     const dim3 g((unsigned)nblk), b(moe::big::NT);
     if constexpr (!GATED) {
       hipLaunchKernelGGL((moe::big::k_gemm<false, 0>), g, b, 0, s, q);

@@ -26,7 +26,9 @@ struct AlignOut {
   float* w_sorted;     // [M] or nullptr
   int32_t* tile_seg;   // [mt_cap] tile -> segment
   int32_t* tile_row0;  // [mt_cap] tile -> first sorted row
-  int32_t* status;     // [4]: bad ids, valid rows, tiles, wait-timeout flag
+  int32_t* status;     // [5]: bad ids, valid rows, tiles, wait-timeout flag, cold segments
+  int32_t* cold_seg;   // [E] segments of 1..cold_max rows, listed apart from the tiles; nullptr = none
+  int32_t cold_max;
   int32_t* sync;       // counters the single-launch decode step expects zero, or nullptr
   int32_t n_sync;
 };
@@ -112,26 +114,38 @@ __device__ int block_exclusive_scan(int32_t* v, int n, int32_t* scratch) {
 }
 
 // After counts (cnt) and start offsets (off) are known: end offsets, the tile
-// table for BM-row tiles, unused perm entries, status.
+// table for BM-row tiles, unused perm entries, status. With o.cold_seg, the
+// segments of 1..o.cold_max rows get no tiles and are listed in o.cold_seg
+// instead (ascending), their number in status[4].
 template <int NT>
 __device__ void finish_tables(const int32_t* cnt, const int32_t* off, int32_t* mt_scan, int E, int M,
                               int total, int BM, int bad, const AlignOut& o, int32_t* scratch) {
   const int tid = threadIdx.x;
+  const int cmax = o.cold_seg ? o.cold_max : 0;
   for (int e = tid; e < E; e += NT) {
     o.counts[e] = cnt[e];
     o.cu[e] = off[e] + cnt[e];
     o.offsets[e] = off[e];
-    mt_scan[e] = (cnt[e] + BM - 1) / BM;
+    mt_scan[e] = cnt[e] <= cmax ? 0 : (cnt[e] + BM - 1) / BM;
   }
   __syncthreads();
   const int n_tiles = block_exclusive_scan<NT>(mt_scan, E, scratch);
   for (int e = tid; e < E; e += NT) {
     const int t0 = mt_scan[e];
-    const int nt = (cnt[e] + BM - 1) / BM;
+    const int nt = cnt[e] <= cmax ? 0 : (cnt[e] + BM - 1) / BM;
     for (int t = 0; t < nt; ++t) {
       o.tile_seg[t0 + t] = e;
       o.tile_row0[t0 + t] = off[e] + t * BM;
     }
+  }
+  int n_cold = 0;
+  if (o.cold_seg) {
+    __syncthreads();  // every thread has read its tile offsets
+    for (int e = tid; e < E; e += NT) mt_scan[e] = (cnt[e] > 0 && cnt[e] <= cmax) ? 1 : 0;
+    __syncthreads();
+    n_cold = block_exclusive_scan<NT>(mt_scan, E, scratch);
+    for (int e = tid; e < E; e += NT)
+      if (cnt[e] > 0 && cnt[e] <= cmax) o.cold_seg[mt_scan[e]] = e;
   }
   for (int p = total + tid; p < M; p += NT) o.perm[p] = -1;
   if (tid == 0) {
@@ -139,6 +153,7 @@ __device__ void finish_tables(const int32_t* cnt, const int32_t* off, int32_t* m
     o.status[1] = total;
     o.status[2] = n_tiles;
     o.status[3] = 0;
+    o.status[4] = n_cold;
   }
 }
 

@@ -393,7 +393,7 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int mt, int nt, int s
 // and each XCD takes a contiguous run of items, so tiles that share weight
 // and row panels share an L2. Blocks past the last item exit.
 template <bool GATED, int AK>
-__global__ __launch_bounds__(NT, 1) void k_gemm(const Params p) {
+__global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_num_vgpr(96))) void k_gemm(const Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem_arr[NS * STAGE_BYTES];
   const int mtl = p.status[2];
   int nsplit = 1;

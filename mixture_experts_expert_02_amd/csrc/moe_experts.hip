@@ -12,12 +12,14 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <mutex>
 
 #include "../../include/moe_experts.h"
 #include "align.hpp"
 #include "combine.hpp"
 #include "gemm_bf16.hpp"
+#include "gemm_cold.hpp"
 #include "gemm_skinny.hpp"
 #include "gemm_mx.hpp"
 #include "decode_prologue.hpp"
@@ -85,6 +87,14 @@ bool use_skinny(const moe_problem& p, long long rows) {
   return p.wfmt == MOE_W_MXFP4 || rows <= 32LL * p.E;
 }
 
+// bf16 prefill problems run their cold segments (at most 32 rows) in the
+// cold-segment kernels beside the tiled kernels unless MOE_EXPERTS_COLD=0
+// (read at every call; tests compare the two).
+bool cold_enabled() {
+  const char* e = std::getenv("MOE_EXPERTS_COLD");
+  return !(e && std::atoi(e) == 0);
+}
+
 struct Plan {
   long long M;   // rows (T*k, or NvS)
   bool skinny;
@@ -105,6 +115,10 @@ struct Plan {
   bool mxbig;
   size_t sa1, sa2, ws1, ws2;
   int NT1, KT1, NT2, KT2;
+  // bf16 prefill: segments of at most moe::cold::MAX_ROWS rows run in the
+  // cold-segment kernels beside the tiled ones (cold_seg: their list)
+  bool cold;
+  size_t cold_seg;
 };
 
 int check_problem(const moe_problem* p, bool grouped) {
@@ -195,6 +209,7 @@ Plan make_plan(const moe_problem& p, bool grouped, size_t ws_bytes = ~(size_t)0)
   pl.s_cap = 1;
   if (!grouped && !pl.skinny && (long long)pl.mt_cap * ceil_div(p.H, moe::big::BN) <= 1024)
     pl.s_cap = std::max(1, std::min(max_split_k(), pl.mxbig ? pl.KT2 : p.I / moe::big::BK));
+  pl.cold = !pl.skinny && !pl.mxbig && p.wfmt == MOE_W_BF16 && cold_enabled();
   pl.fused_align = !grouped && pl.M <= kFusedMaxRows && p.E <= kFusedMaxExperts;
   if (!grouped && !pl.fused_align) {
     pl.chunk = (int)std::max<long long>(512, (ceil_div(pl.M, 256) + 63) / 64 * 64);
@@ -206,12 +221,13 @@ Plan make_plan(const moe_problem& p, bool grouped, size_t ws_bytes = ~(size_t)0)
     o = up(o + bytes);
     return at;
   };
-  pl.status = take(16);
+  pl.status = take(32);
   pl.counts = take(4ull * p.E);
   pl.cu = take(4ull * p.E);
   pl.offsets = take(4ull * p.E);
   pl.tile_seg = take(4ull * std::max(pl.mt_cap, 1));
   pl.tile_row0 = take(4ull * std::max(pl.mt_cap, 1));
+  if (pl.cold) pl.cold_seg = take(4ull * p.E);
   if (!grouped) {
     if (!pl.fused_align) {
       pl.blkcnt = take(4ull * pl.nch * p.E);
@@ -321,6 +337,32 @@ int device_cus(int* n) {
 int launch_status() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// A second stream per device for the cold-segment kernels, with the two
+// events that fork it from the caller's stream and join it back; created on
+// first use with the default priority, kept until the process ends. The
+// fork / join calls of one forward are made under the mutex, so forwards
+// issued from several host threads do not interleave their event records.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+int side_stream(SideStream** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
+  SideStream& ss = g_side[dev];
+  if (!ss.stream) {
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess) return MOE_EHIP;
+    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      return MOE_EHIP;
+  }
+  *out = &ss;
+  return MOE_OK;
 }
 
 // ---------------------------------------------------------------- align
@@ -518,6 +560,75 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     }
   }
   return launch_status();
+}
+
+// The cold segments' GEMM (gemm_cold.hpp): one workgroup per compute unit.
+template <bool GATED>
+int launch_cold(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws, hipStream_t s) {
+  moe::cold::Params q;
+  q.A = (const uint16_t*)io.A;
+  q.a_perm = io.a_perm;
+  q.a_div = io.a_div;
+  q.B0 = (const uint16_t*)io.B0;
+  q.B1 = (const uint16_t*)io.B1;
+  q.N = io.N;
+  q.K = io.K;
+  q.cold_seg = at<int32_t>(ws, pl.cold_seg);
+  q.seg_end = at<int32_t>(ws, pl.cu);
+  q.status = at<int32_t>(ws, pl.status);
+  q.n_tiles = ceil_div(io.N, moe::cold::block_cols(GATED));
+  q.C = (uint16_t*)io.C;
+  q.row_w = io.row_w;
+  q.act = act_params(p);
+  q.ep = expert_params(p);
+  q.c_split = io.c_split;
+  q.s_cap = GATED ? 1 : io.s_cap;
+  q.tiled_cols = ceil_div(io.N, moe::big::BN);
+  q.tiled_kt = io.K / moe::big::BK;
+  const int rc = device_cus(&q.ncu);
+  if (rc) return rc;
+  const dim3 g((unsigned)q.ncu), b(moe::cold::NT);
+  if constexpr (!GATED) {
+    hipLaunchKernelGGL((moe::cold::k_cold<false, 0>), g, b, 0, s, q);
+  } else {
+    if (p.act == MOE_ACT_SWIGLU_OAI) hipLaunchKernelGGL((moe::cold::k_cold<true, 1>), g, b, 0, s, q);
+    else if (p.act == MOE_ACT_SITU) hipLaunchKernelGGL((moe::cold::k_cold<true, 2>), g, b, 0, s, q);
+    else hipLaunchKernelGGL((moe::cold::k_cold<true, 0>), g, b, 0, s, q);
+  }
+  return launch_status();
+}
+
+// GEMM1 then GEMM2 of the tiled segments on s and, with a cold-segment list,
+// the cold segments' GEMM1 then GEMM2 on the side stream (forked from s after
+// everything before, joined back before what follows), or on s itself when
+// side is false. The tiled GEMM1 is issued first, so its workgroups take the
+// compute units; the cold kernels' workgroups fit beside them.
+int launch_gemms(const moe_problem& p, const Plan& pl, const GemmIO& g1, const GemmIO& g2, void* ws, hipStream_t s,
+                 bool side, const std::function<void(int)>& mark) {
+  int rc;
+  if (!pl.cold) {
+    if ((rc = launch_gemm<true>(p, pl, g1, ws, s))) return rc;
+    mark(2);
+    if ((rc = launch_gemm<false>(p, pl, g2, ws, s))) return rc;
+    return MOE_OK;
+  }
+  if (!side) {
+    if ((rc = launch_gemm<true>(p, pl, g1, ws, s)) || (rc = launch_cold<true>(p, pl, g1, ws, s))) return rc;
+    mark(2);
+    if ((rc = launch_gemm<false>(p, pl, g2, ws, s)) || (rc = launch_cold<false>(p, pl, g2, ws, s))) return rc;
+    return MOE_OK;
+  }
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* ss = nullptr;
+  if ((rc = side_stream(&ss))) return rc;
+  if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess)
+    return MOE_EHIP;
+  if ((rc = launch_gemm<true>(p, pl, g1, ws, s)) || (rc = launch_cold<true>(p, pl, g1, ws, ss->stream))) return rc;
+  mark(2);
+  if ((rc = launch_gemm<false>(p, pl, g2, ws, s)) || (rc = launch_cold<false>(p, pl, g2, ws, ss->stream))) return rc;
+  if (hipEventRecord(ss->join, ss->stream) != hipSuccess || hipStreamWaitEvent(s, ss->join, 0) != hipSuccess)
+    return MOE_EHIP;
+  return MOE_OK;
 }
 
 // Workgroups of kernel f (NT threads, dyn bytes of dynamic LDS) that fit on
@@ -720,7 +831,7 @@ int check_common_ptrs(const moe_problem* p, const void* x, const void* wg, const
 
 int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const float* tw, const void* wg,
                  const void* wu, const void* wd, const uint8_t* sg, const uint8_t* su, const uint8_t* sd,
-                 void* out, void* ws, size_t ws_bytes, hipStream_t s, void* const* ev, int n_ev) {
+                 void* out, void* ws, size_t ws_bytes, hipStream_t s, void* const* ev, int n_ev, bool side) {
   int rc = check_problem(p, false);
   if (rc) return rc;
   if (!ids || !tw) return MOE_EINVAL;
@@ -732,10 +843,14 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
   if (ws_bytes < pl.total) return MOE_ENOSPC;
   if ((rc = set_attrs())) return rc;
   auto mark = [&](int i) {
-    if (n_ev) hipEventRecord((hipEvent_t)ev[i], s);
+    if (n_ev) (void)hipEventRecord((hipEvent_t)ev[i], s);
   };
 
   moe::AlignOut o{};
+  if (pl.cold) {
+    o.cold_seg = at<int32_t>(ws, pl.cold_seg);
+    o.cold_max = moe::cold::MAX_ROWS;
+  }
   o.counts = at<int32_t>(ws, pl.counts);
   o.cu = at<int32_t>(ws, pl.cu);
   o.offsets = at<int32_t>(ws, pl.offsets);
@@ -808,10 +923,14 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
     if (p->weight_on_input) launch_quant(mx8, g1.A, pl.M, p->H, g1.Aq, s);
     else launch_quant(mx8, x, pl.M, p->H, g1.Aq, s, o.perm, p->k, o.status);
   }
-  if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
-  mark(2);
-  if (mx && !mx8) launch_quant(false, g2.A, pl.M, p->I, g2.Aq, s);
-  if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
+  if (mx) {
+    if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
+    mark(2);
+    if (!mx8) launch_quant(false, g2.A, pl.M, p->I, g2.Aq, s);
+    if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
+  } else if ((rc = launch_gemms(*p, pl, g1, g2, ws, s, side, mark))) {
+    return rc;
+  }
 
   mark(3);
   moe::SplitSum ss{o.status, ceil_div(p->H, moe::big::BN), p->I / moe::big::BK, 1, pl.s_cap, y_split};
@@ -857,7 +976,7 @@ int moe_experts_forward(const moe_problem* p, const void* x, const int32_t* topk
                         const uint8_t* s_up, const uint8_t* s_down, void* out, void* workspace,
                         size_t workspace_bytes, moe_stream_t stream) {
   return forward_impl(p, x, topk_ids, topk_weights, w_gate, w_up, w_down, s_gate, s_up, s_down, out, workspace,
-                      workspace_bytes, (hipStream_t)stream, nullptr, 0);
+                      workspace_bytes, (hipStream_t)stream, nullptr, 0, true);
 }
 
 int moe_experts_forward_timed(const moe_problem* p, const void* x, const int32_t* topk_ids,
@@ -866,7 +985,7 @@ int moe_experts_forward_timed(const moe_problem* p, const void* x, const int32_t
                               void* workspace, size_t workspace_bytes, moe_stream_t stream,
                               void* const* stage_events, int n_events) {
   return forward_impl(p, x, topk_ids, topk_weights, w_gate, w_up, w_down, s_gate, s_up, s_down, out, workspace,
-                      workspace_bytes, (hipStream_t)stream, stage_events, n_events);
+                      workspace_bytes, (hipStream_t)stream, stage_events, n_events, true);
 }
 
 int moe_experts_forward_noalloc(const moe_problem* p, const void* x, const int32_t* topk_ids,
@@ -879,8 +998,10 @@ int moe_experts_forward_noalloc(const moe_problem* p, const void* x, const int32
   void* ws = nullptr;
   const int r = scratch_on_device(&ws);
   if (r) return r;
+  // no second stream here (creating one allocates); the cold kernels follow
+  // the tiled ones on the caller's stream
   return forward_impl(p, x, topk_ids, topk_weights, w_gate, w_up, w_down, s_gate, s_up, s_down, out, ws,
-                      kScratchBytes, (hipStream_t)stream, nullptr, 0);
+                      kScratchBytes, (hipStream_t)stream, nullptr, 0, false);
 }
 
 size_t moe_align_workspace_bytes(int32_t T, int32_t k, int32_t E) {
@@ -949,11 +1070,15 @@ int grouped_impl(const moe_problem* p, const void* x_nvs, const int32_t* cu_seql
   if (workspace_bytes < pl.total) return MOE_ENOSPC;
   if ((rc = set_attrs())) return rc;
   auto mark = [&](int i) {
-    if (n_ev) hipEventRecord((hipEvent_t)ev[i], s);
+    if (n_ev) (void)hipEventRecord((hipEvent_t)ev[i], s);
   };
   void* ws = workspace;
   mark(0);
   moe::AlignOut o{};
+  if (pl.cold) {
+    o.cold_seg = at<int32_t>(ws, pl.cold_seg);
+    o.cold_max = moe::cold::MAX_ROWS;
+  }
   o.counts = at<int32_t>(ws, pl.counts);
   o.cu = at<int32_t>(ws, pl.cu);
   o.offsets = at<int32_t>(ws, pl.offsets);
@@ -979,15 +1104,17 @@ int grouped_impl(const moe_problem* p, const void* x_nvs, const int32_t* cu_seql
     g1.Aq = quant_rows_at(ws, pl.xq, pl.M, p->H);
     launch_quant(mx8, g1.A, pl.M, p->H, g1.Aq, s);
   }
-  if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
   GemmIO g2{at<void>(ws, pl.act), nullptr, 1, w_down, nullptr, s_down, nullptr, p->H, p->I, out_nvs, nullptr, 1, 0, {},
             {}};
-  mark(2);
   if (mx) {
+    if ((rc = launch_gemm<true>(*p, pl, g1, ws, s))) return rc;
+    mark(2);
     g2.Aq = quant_rows_at(ws, pl.aq, pl.M, p->I);
     if (!mx8) launch_quant(false, g2.A, pl.M, p->I, g2.Aq, s);
+    if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
+  } else if ((rc = launch_gemms(*p, pl, g1, g2, ws, s, true, mark))) {
+    return rc;
   }
-  if ((rc = launch_gemm<false>(*p, pl, g2, ws, s))) return rc;
   mark(3);
   hipLaunchKernelGGL(moe::k_zero_tail, dim3(p->T), dim3(256), 0, s, (uint16_t*)out_nvs,
                      (const int32_t*)o.status, p->T, p->H);

@@ -205,6 +205,29 @@ def test_workspace_reuse_with_smaller_T():
         assert rel_err(to_np(out), ref) <= TOL
 
 
+# ------------------------------------------------------------------ cold segments
+# Segments of 1..32 rows run in the cold-segment kernels beside the 256-row
+# tiles (MOE_EXPERTS_COLD=0 keeps them in the tiles): both against the oracle,
+# with the down projection's K split into partial outputs or not.
+@pytest.mark.parametrize("cold", ["1", "0"])
+@pytest.mark.parametrize("max_split", ["1", "4"])
+def test_cold_segments_match_oracle(cold, max_split, monkeypatch):
+    monkeypatch.setenv("MOE_EXPERTS_COLD", cold)
+    monkeypatch.setenv("MOE_EXPERTS_MAX_SPLIT_K", max_split)
+    T, H, I, E, k = 600, 192, 320, 24, 2
+    print(f"[forward] cold={cold} split<={max_split} T={T} H={H} I={I} E={E} k={k}", flush=True)
+    x, ids, w, W, S = make_problem(21, T, H, I, E, k, "bf16", skew=1.3)
+    n = np.bincount(ids.ravel(), minlength=E)
+    assert np.any((n > 0) & (n <= 16)) and np.any((n > 16) & (n <= 32)) and np.any(n > 256)
+    for act in ("silu", "swiglu_oai"):
+        act_kw = dict(act=act, **ACT_PARAMS[act])
+        out = run_gpu(x, ids, w, W, S, act_kw)
+        err = rel_err(to_np(out), oracle_out(x, ids, w, W, S, act_kw))
+        print(f"[forward] cold={cold} split<={max_split} {act} rel err {err:.2e}", flush=True)
+        assert err <= TOL
+        assert torch.equal(out, run_gpu(x, ids, w, W, S, act_kw))
+
+
 # ------------------------------------------------------------------ pre-grouped entry
 def grouped_case(seed, lengths, tail, H=256, I=384, wfmt="bf16"):
     rng = np.random.default_rng(seed)
@@ -225,6 +248,7 @@ def grouped_case(seed, lengths, tail, H=256, I=384, wfmt="bf16"):
 
 @pytest.mark.parametrize("lengths,tail,wfmt,on_input", [
     ([300, 0, 257, 1, 0, 512, 40], 13, "bf16", False),     # empty segments, ragged, padding rows
+    ([400, 3, 32, 0, 17, 33, 290, 16], 6, "bf16", False),  # cold segments (1..32 rows) beside tiled ones
     ([0, 0, 5, 0], 7, "bf16", False),                      # decode-sized (weight-streaming path)
     ([33, 0, 70, 2], 5, "mxfp4", False),
     ([600, 600], 0, "bf16", False),

@@ -142,10 +142,12 @@ class HipEvents:
 
 def kernel_source_hash(kind: str) -> str:
     """sha256 of the sources a GEMM1 kernel is built from (bf16: the prefill
-    GEMM; mxfp4: the decode GEMM; mx_prefill: the block-scaled prefill GEMM)."""
+    GEMM, with the align that leaves the cold segments out of its tiles and
+    the cold-segment kernel beside it; mxfp4: the decode GEMM; mx_prefill: the
+    block-scaled prefill GEMM)."""
     import hashlib
     h = hashlib.sha256()
-    files = {"bf16": ("common.hpp", "gemm_bf16.hpp"), "mxfp4": ("common.hpp", "gemm_skinny.hpp"),
+    files = {"bf16": ("common.hpp", "align.hpp", "gemm_bf16.hpp", "gemm_cold.hpp"), "mxfp4": ("common.hpp", "gemm_skinny.hpp"),
              "mx_prefill": ("common.hpp", "gemm_bf16.hpp", "gemm_mx.hpp")}[kind]
     for f in files:
         with open(os.path.join(ROOT, "mixture_experts_expert_02_amd", "csrc", f), "rb") as fh:

@@ -126,6 +126,18 @@ typedef struct {
   const float* limit_e;
   const float* fc1_alpha;
   const float* fc2_alpha;
+  /* MXFP4 weights with MXFP8 activations: the weights in the prefill
+   * kernels' own format, written by moe_mx_pack_weights from the same
+   * w_gate / w_up / w_down and scales (device, 16-byte aligned), or NULL (the
+   * zero-initialised default). flashinfer_moe_ep page,
+   * process_weights_after_loading: the weights are put into the kernel's
+   * format once, before the first forward. When set, the token-major prefill
+   * path reads the weights from here and skips the per-call transpose of
+   * their scales; the canonical tensors are still required (the decode
+   * kernels and the pre-grouped entry read them). The library cannot tell a
+   * stale packing from a fresh one: re-pack after changing the weights. Set
+   * with any other weight or activation format: MOE_EINVAL. */
+  const void* mx_packed;
 } moe_problem;
 
 /* Byte offsets of the intermediates inside a forward workspace (for tests and
@@ -174,6 +186,29 @@ typedef struct {
                         * 1024, 4 bytes per tile row holding the scales of its column
                         blocks 4g, 4g+2, 4g+1, 4g+3 in that order (0 past I / 32) */
 } moe_ws_layout;
+
+/* Bytes of the packed weights (moe_problem.mx_packed) of problem p: for
+ * each expert, column tile and 128-K stage of GEMM1 (ceil(I / 128) column
+ * tiles of 128 gate and the same 128 up rows, ceil(H / 128) stages) and of
+ * GEMM2 (ceil(H / 256) tiles of 256 down rows, ceil(I / 128) stages), one
+ * 17408-byte block: 256 rows x 64 bytes of e2m1 codes (row r's 16-byte chunk
+ * c at r * 64 + 16 (c ^ ((r >> 2) & 3)); codes past N or past K are 0), then
+ * the rows' 1 KB e8m0 scale block (row r's four block scales of the stage at
+ * r * 4 in the order 0, 2, 1, 3; blocks past K are 0, rows past N repeat row
+ * N - 1's). GEMM1's blocks for all experts, then GEMM2's; within an expert
+ * column tile major. 0 when p is invalid or not MXFP4 x MXFP8.
+ * flashinfer_moe_ep page, process_weights_after_loading. */
+size_t moe_mx_packed_bytes(const moe_problem* p);
+
+/* Writes the packed weights of problem p (moe_mx_packed_bytes bytes) into
+ * packed (device, 16-byte aligned, caller-owned) from the canonical MXFP4
+ * tensors (the moe_experts_forward arguments of the same names), on stream;
+ * asynchronous like the forward. Host-side errors before any launch:
+ * MOE_EINVAL (invalid p, not MXFP4 x MXFP8, a NULL or misaligned pointer),
+ * MOE_ENOSPC (packed_bytes below moe_mx_packed_bytes). */
+int moe_mx_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up, const void* w_down,
+                        const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down, void* packed,
+                        size_t packed_bytes, moe_stream_t stream);
 
 /* Workspace bytes a moe_experts_forward call on problem *p needs (0 if *p is
  * invalid). Depends only on the sizes in *p, so a workspace sized once for the

@@ -65,6 +65,19 @@ constexpr int STAGE = A_BYTES + B_BYTES + 2 * SC_BYTES;
 constexpr int LOADS = 7;                // load instructions per wave and stage
 constexpr uint32_t kNoLoad = 0x80000000u;  // buffer offset past any operand: reads 0
 
+// Packed weights (moe_mx_pack_weights): the kernel's format, made once for a
+// set of weights (flashinfer_moe_ep page, process_weights_after_loading: the
+// weights are put into the kernel's format before the first forward). For
+// each expert, column tile and stage, one PK_STAGE-byte block that is the
+// stage's LDS image of the B operand: 256 rows x 64 bytes of e2m1 codes, row
+// r's 16-byte chunk c at r * 64 + 16 (c ^ ((r >> 2) & 3)) (GEMM1: rows 0-127
+// gate rows n0.., 128-255 the same up rows; codes past N or past K are 0),
+// then the 1 KB scale block of those rows (as k_mx_prep makes it). A wave's
+// load of 16 rows is then one contiguous 1 KB, whole 128-byte lines, where
+// the [E, N, K/2] layout gives 16 rows x 64 bytes. Blocks run column tile
+// major, stage minor, expert by expert: GEMM1's experts, then GEMM2's.
+constexpr int PK_STAGE = B_BYTES + SC_BYTES;
+
 // position of block b (0..3) of a stage inside a row's 4 scale bytes
 __host__ __device__ constexpr int sc_pos(int b) { return ((b & 1) << 1) | (b >> 1); }
 
@@ -79,6 +92,8 @@ struct Params {
   const uint8_t* B0;       // e2m1 codes [G, N, K/2] (gate or down)
   const uint8_t* B1;       // (up) for GEMM1
   const uint8_t* B_sc;     // scale blocks [G][n_tiles][KT]
+  const uint8_t* Bp;       // packed weights of this GEMM (codes and scale blocks), or nullptr: B0/B1/B_sc
+  uint32_t bp_expert;      // bytes of one expert's packed blocks (n_tiles x KT x PK_STAGE)
   int32_t N, K, KT;        // KT = ceil(K / BK); K is a multiple of 64
   const int32_t* tile_seg;
   const int32_t* tile_row0;
@@ -165,6 +180,16 @@ __device__ __forceinline__ void mx_tile_ctx(const Params& p, int item, int mtl, 
     int arow = first;
     if (r < t.rows) arow = p.a_perm ? p.a_perm[t.row0 + r] / p.a_div : t.row0 + r;
     t.a_off[i] = r < t.rows ? (uint32_t)arow * (uint32_t)K + (uint32_t)(st_lo * BK + chunk * 16) : kNoLoad;
+  }
+  if (p.Bp) {
+    // packed: this tile's first stage block, rows 32 wave + 16 j .. of it
+    const uint32_t blk = (uint32_t)(t.nt * p.KT + st_lo) * PK_STAGE;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) t.b_off[j] = blk + (uint32_t)((wave * 32 + j * 16) * 64 + lane * 16);
+    t.bbase = p.Bp + (size_t)t.seg * p.bp_expert;
+    t.sc_src = wave < 4 ? p.A_sc + ((size_t)t.mt * p.KT + st_lo) * SC_BYTES + wave * 256
+                        : t.bbase + blk + B_BYTES + (wave - 4) * 256;
+    return;
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -334,7 +359,11 @@ __device__ __forceinline__ void mx_gemm(const Params& p, lds_u8* smem) {
   if (item >= hi) return;
 
   const __amdgpu_buffer_rsrc_t rsA = operand_rsrc(p.A, p.a_bytes);
-  const uint32_t wbytes = (uint32_t)N * ((uint32_t)p.K / 2);
+  // weight codes: one expert's [N, K/2] rows, or its packed blocks; the
+  // stride of a stage in them, and in the scale blocks a wave copies
+  const uint32_t wbytes = p.Bp ? p.bp_expert : (uint32_t)N * ((uint32_t)p.K / 2);
+  const uint32_t b_stage = p.Bp ? (uint32_t)PK_STAGE : (uint32_t)(BK / 2);
+  const uint32_t sc_stage = (p.Bp && wave >= 4) ? (uint32_t)PK_STAGE : (uint32_t)SC_BYTES;
   MxTile cur, nxt;
   mx_tile_ctx<GATED>(p, item, mtl, nsplit, wave, lane, cur);
   bool has_next = item + S < hi;
@@ -368,9 +397,9 @@ __device__ __forceinline__ void mx_gemm(const Params& p, lds_u8* smem) {
     } else if ((q) < 6) {                                                                                      \
       const __amdgpu_buffer_rsrc_t rsB = operand_rsrc(in_cur ? cur.bbase : nxt.bbase, wbytes);                 \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (__attribute__((address_space(3))) void*)(dst + A_BYTES + (wave * 32 + ((q) - 4) * 16) * 64), \
-                                               16, ((in_cur ? cur.b_off[(q) & 1] : nxt.b_off[(q) & 1]) + (uint32_t)u * (BK / 2)) | kill, 0, 0, 0); \
+                                               16, ((in_cur ? cur.b_off[(q) & 1] : nxt.b_off[(q) & 1]) + (uint32_t)u * b_stage) | kill, 0, 0, 0); \
     } else if (lane < 16) {                                                                                    \
-      __builtin_amdgcn_global_load_lds((in_cur ? cur.sc_src : nxt.sc_src) + (size_t)min(u, ktx - 1) * SC_BYTES + lane * 16, \
+      __builtin_amdgcn_global_load_lds((in_cur ? cur.sc_src : nxt.sc_src) + (size_t)min(u, ktx - 1) * sc_stage + lane * 16, \
                                        (__attribute__((address_space(3))) void*)(dst + A_BYTES + B_BYTES + wave * 256), 16, 0, 0); \
     }                                                                                                          \
   }
@@ -689,6 +718,53 @@ __global__ __launch_bounds__(256) void k_mx_prep(const PrepParams q) {
     }
     *(uint32_t*)(dst + (size_t)u * SC_BYTES) = w;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Packing (moe_mx_pack_weights): one workgroup per packed block (expert,
+// column tile, stage; GEMM1's blocks first), thread r writing row r's 64 code
+// bytes in the swizzled order and its 4 scale bytes. Made once per set of
+// weights, not per call.
+struct PackParams {
+  const uint8_t* Wg;   // e2m1 codes [E, I, H/2]
+  const uint8_t* Wu;
+  const uint8_t* Wd;   // [E, H, I/2]
+  const uint8_t* Sg;   // e8m0 [E, I, H/32]
+  const uint8_t* Su;
+  const uint8_t* Sd;   // [E, H, I/32]
+  uint8_t* out;
+  int32_t E, H, I;
+  int32_t NT1, KT1, NT2, KT2;
+};
+
+__global__ __launch_bounds__(256) void k_mx_pack(const PackParams q) {
+  const int r = threadIdx.x;
+  int b = blockIdx.x;
+  const int n1 = q.E * q.NT1 * q.KT1;
+  const bool g1 = b < n1;
+  if (!g1) b -= n1;
+  const int NTc = g1 ? q.NT1 : q.NT2, KT = g1 ? q.KT1 : q.KT2;
+  const int e = b / (NTc * KT), rem = b - e * (NTc * KT);
+  const int nt = rem / KT, u = rem - nt * KT;
+  const int N = g1 ? q.I : q.H, K = g1 ? q.H : q.I;
+  const int KB2 = K / 2, KB = K / 32;
+  const int n = g1 ? nt * 128 + (r & 127) : nt * 256 + r;  // weight row of tile row r
+  const uint8_t* W = g1 ? (r < 128 ? q.Wg : q.Wu) : q.Wd;
+  const uint8_t* S = g1 ? (r < 128 ? q.Sg : q.Su) : q.Sd;
+  uint8_t* blk = q.out + ((size_t)(g1 ? 0 : n1) + ((size_t)e * NTc + nt) * KT + u) * PK_STAGE;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int kb = u * (BK / 2) + c * 16;  // byte of the row
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < N && kb < KB2) v = *(const u32x4*)(W + ((size_t)e * N + n) * KB2 + kb);
+    *(u32x4*)(blk + r * 64 + 16 * (c ^ ((r >> 2) & 3))) = v;
+  }
+  // rows past N repeat row N - 1's scales (their codes are 0), blocks past K are 0
+  const uint8_t* srow = S + ((size_t)e * N + min(n, N - 1)) * KB;
+  uint32_t sv[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) sv[t] = 4 * u + t < KB ? srow[4 * u + t] : 0u;
+  *(uint32_t*)(blk + B_BYTES + r * 4) = order_0213(sv[0], sv[1], sv[2], sv[3]);
 }
 
 }  // namespace mx

@@ -138,6 +138,8 @@ int check_problem(const moe_problem* p, bool grouped) {
   if (p->weight_on_input != 0 && p->weight_on_input != 1) return MOE_EINVAL;
   if (p->a_fmt != MOE_A_BF16 && p->a_fmt != MOE_A_MXFP8) return MOE_EINVAL;
   if (p->a_fmt == MOE_A_MXFP8 && p->wfmt != MOE_W_MXFP4) return MOE_ENOTSUP;  // block-scaled MFMA path only
+  if (p->mx_packed && (p->wfmt != MOE_W_MXFP4 || p->a_fmt != MOE_A_MXFP8 || !aligned16(p->mx_packed)))
+    return MOE_EINVAL;
   const void* ep[] = {p->alpha_e, p->beta_e, p->limit_e, p->fc1_alpha, p->fc2_alpha};
   for (const void* q : ep)
     if (((uintptr_t)q & 3u) != 0) return MOE_EINVAL;
@@ -188,6 +190,15 @@ int max_split_k() {
 // workspace sized for a larger T (fewer K ranges, more rows) still serves.
 size_t quant_bytes(long long R, int K) {
   return (size_t)R * (2ull * K + moe::skinny::quant_sc_stride(K));
+}
+
+// Packed MXFP4 x MXFP8 prefill weights: bytes of one expert's GEMM1 blocks
+// and of one expert's GEMM2 blocks (gemm_mx.hpp, PK_STAGE).
+size_t mx_packed_expert1(const moe_problem& p) {
+  return (size_t)ceil_div(p.I, moe::mx::BN / 2) * ceil_div(p.H, moe::mx::BK) * moe::mx::PK_STAGE;
+}
+size_t mx_packed_expert2(const moe_problem& p) {
+  return (size_t)ceil_div(p.H, moe::mx::BN) * ceil_div(p.I, moe::mx::BK) * moe::mx::PK_STAGE;
 }
 
 Plan make_plan(const moe_problem& p, bool grouped, size_t ws_bytes = ~(size_t)0) {
@@ -735,7 +746,8 @@ int forward_mx(const moe_problem& p, const Plan& pl, const void* x, const moe::A
   pp.status = o.status;
   pp.mt_cap = pl.mt_cap;
   pp.SA1 = at<uint8_t>(ws, pl.sa1);
-  const long long nprep = (long long)p.E * (pl.NT1 + pl.NT2) + pl.mt_cap;
+  if (p.mx_packed) pp.E = 0;  // the packed blocks carry the weights' scale blocks
+  const long long nprep = (long long)pp.E * (pl.NT1 + pl.NT2) + pl.mt_cap;
   if (nprep > 0x7fffffffLL) return MOE_ENOTSUP;
   hipLaunchKernelGGL(moe::mx::k_mx_prep, dim3((unsigned)nprep), dim3(256),
                      (size_t)moe::mx::prep_lds_bytes(std::max(p.H, p.I)), s, pp);
@@ -753,6 +765,8 @@ int forward_mx(const moe_problem& p, const Plan& pl, const void* x, const moe::A
   g.B0 = (const uint8_t*)wg;
   g.B1 = (const uint8_t*)wu;
   g.B_sc = pp.WS1;
+  g.Bp = (const uint8_t*)p.mx_packed;
+  g.bp_expert = (uint32_t)mx_packed_expert1(p);
   g.N = p.I;
   g.K = p.H;
   g.KT = pl.KT1;
@@ -795,6 +809,8 @@ int forward_mx(const moe_problem& p, const Plan& pl, const void* x, const moe::A
   g2.B0 = (const uint8_t*)wd;
   g2.B1 = nullptr;
   g2.B_sc = at<uint8_t>(ws, pl.ws2);
+  g2.Bp = p.mx_packed ? (const uint8_t*)p.mx_packed + (size_t)p.E * mx_packed_expert1(p) : nullptr;
+  g2.bp_expert = (uint32_t)mx_packed_expert2(p);
   g2.N = p.H;
   g2.K = p.I;
   g2.KT = pl.KT2;
@@ -944,6 +960,43 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
 }  // namespace
 
 extern "C" {
+
+size_t moe_mx_packed_bytes(const moe_problem* p) {
+  if (check_problem(p, false)) return 0;
+  if (p->wfmt != MOE_W_MXFP4 || p->a_fmt != MOE_A_MXFP8) return 0;
+  return (size_t)p->E * (mx_packed_expert1(*p) + mx_packed_expert2(*p));
+}
+
+int moe_mx_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up, const void* w_down,
+                        const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down, void* packed,
+                        size_t packed_bytes, moe_stream_t stream) {
+  if (check_problem(p, false)) return MOE_EINVAL;
+  if (p->wfmt != MOE_W_MXFP4 || p->a_fmt != MOE_A_MXFP8) return MOE_EINVAL;
+  const void* ptrs[] = {w_gate, w_up, w_down, s_gate, s_up, s_down, packed};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return MOE_EINVAL;
+  if (packed_bytes < moe_mx_packed_bytes(p)) return MOE_ENOSPC;
+  moe::mx::PackParams q;
+  q.Wg = (const uint8_t*)w_gate;
+  q.Wu = (const uint8_t*)w_up;
+  q.Wd = (const uint8_t*)w_down;
+  q.Sg = s_gate;
+  q.Su = s_up;
+  q.Sd = s_down;
+  q.out = (uint8_t*)packed;
+  q.E = p->E;
+  q.H = p->H;
+  q.I = p->I;
+  q.NT1 = ceil_div(p->I, moe::mx::BN / 2);
+  q.KT1 = ceil_div(p->H, moe::mx::BK);
+  q.NT2 = ceil_div(p->H, moe::mx::BN);
+  q.KT2 = ceil_div(p->I, moe::mx::BK);
+  const long long nblk = (long long)p->E * ((long long)q.NT1 * q.KT1 + (long long)q.NT2 * q.KT2);
+  if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
+  if (nblk == 0) return MOE_OK;
+  hipLaunchKernelGGL(moe::mx::k_mx_pack, dim3((unsigned)nblk), dim3(256), 0, (hipStream_t)stream, q);
+  return launch_status();
+}
 
 size_t moe_experts_workspace_bytes(const moe_problem* p) {
   if (check_problem(p, false)) return 0;

@@ -190,3 +190,66 @@ def test_mx_prefill_quantized_rows(shape):
     print(f"[mx_prefill] epilogue quantization: {int((sc != want).sum())} of {sc.size} scale codes and "
           f"{int(diff.sum())} of {diff.size} elements differ from the oracle's own decisions (all within the "
           f"kernels' fp32 error bound)", flush=True)
+
+
+# ------------------------------------------------------------------ packed weights
+def host_pack(W, S, H, I):
+    """The packed layout of moe_mx_pack_weights, written out on the host from
+    the header's description (test infrastructure, not the oracle)."""
+    E = W[0].shape[0]
+    out = []
+    for g1, N, K in ((True, I, H), (False, H, I)):
+        KT = -(-K // 128)
+        NTc = -(-N // 128) if g1 else -(-N // 256)
+        mats = [(W[0].numpy(), S[0].numpy()), (W[1].numpy(), S[1].numpy())] if g1 else [(W[2].numpy(), S[2].numpy())]
+        for e in range(E):
+            for nt in range(NTc):
+                for u in range(KT):
+                    blk = np.zeros(17408, dtype=np.uint8)
+                    for r in range(256):
+                        c_mat, s_mat = mats[r // 128] if g1 else mats[0]
+                        n = nt * 128 + (r & 127) if g1 else nt * 256 + r
+                        for c in range(4):
+                            kb = u * 64 + c * 16
+                            if n < N and kb < K // 2:
+                                slot = c ^ ((r >> 2) & 3)
+                                blk[r * 64 + 16 * slot: r * 64 + 16 * slot + 16] = c_mat[e, n, kb:kb + 16]
+                        srow = s_mat[e, min(n, N - 1)]
+                        v = [srow[4 * u + t] if 4 * u + t < K // 32 else 0 for t in range(4)]
+                        blk[16384 + r * 4: 16384 + r * 4 + 4] = [v[0], v[2], v[1], v[3]]
+                    out.append(blk)
+    return np.concatenate(out)
+
+
+def test_mx_pack_layout_matches_host_packer():
+    """moe_mx_pack_weights byte for byte against the layout the header
+    describes: K with a half stage (H = 320), N with a half column tile
+    (I = 192: rows past N are zero), two experts."""
+    T, H, I, E, k = 64, 320, 192, 2, 2
+    _, _, _, W, S = make_problem(77, T, H, I, E, k, "mxfp4")
+    p = B.problem(T, H, I, E, k, "mxfp4", "swiglu_oai", act_fmt="mxfp8")
+    packed = B.mx_pack_weights(p, *[t.to(DEV) for t in W], *[t.to(DEV) for t in S])
+    torch.cuda.synchronize()
+    want = host_pack(W, S, H, I)
+    assert packed.numel() == want.size == B.moe_mx_packed_bytes(p)
+    got = packed.cpu().numpy()
+    assert np.array_equal(got, want), f"{int((got != want).sum())} bytes differ"
+
+
+@pytest.mark.parametrize("name,shape,act,extra", [CASES[0], CASES[1], CASES[3], CASES[6]],
+                         ids=[CASES[i][0] for i in (0, 1, 3, 6)])
+def test_mx_prefill_packed_weights_bitwise(name, shape, act, extra):
+    """With the packed weights the GEMMs read the same bytes in the same
+    order: outputs bit for bit equal to the unpacked path."""
+    T, H, I, E, k = shape
+    print(f"[mx_prefill] packed weights {name} T={T} H={H} I={I} E={E} k={k}", flush=True)
+    x, ids, w, W, S, act_kw = problem_for(name, shape, act, extra)
+    Wd, Sd = [t.to(DEV) for t in W], [t.to(DEV) for t in S]
+    kw = {kk: v for kk, v in act_kw.items() if kk in ("act", "alpha", "beta", "limit", "weight_on_input")}
+    p = B.problem(T, H, I, E, k, "mxfp4", act_fmt="mxfp8", **kw)
+    packed = B.mx_pack_weights(p, *Wd, *Sd)
+    xd, idd, wd = x.to(DEV), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
+    a = B.experts_forward(xd, idd, wd, *Wd, scales=Sd, **act_kw)
+    b = B.experts_forward(xd, idd, wd, *Wd, scales=Sd, mx_packed=packed, **act_kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

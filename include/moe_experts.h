@@ -36,7 +36,18 @@
  *     consecutive K elements (OCP Microscaling v1.0).
  *   - The caller owns every buffer, including the workspace. The library never
  *     allocates, frees or synchronises inside a forward call: it only enqueues
- *     kernels on `stream` (a hipStream_t; NULL = the default stream).
+ *     kernels on `stream` (a hipStream_t; NULL = the default stream). One
+ *     exception to "on `stream`": the forwards of bf16 prefill problems run
+ *     the kernels of their segments of at most 32 rows on a second stream
+ *     that the library creates once per device (non-blocking, default
+ *     priority), forked from `stream` and joined back into it with events
+ *     inside the call, so that to the caller the work is ordered as if all
+ *     of it ran on `stream`, and capturing `stream` into a HIP graph
+ *     captures both. That stream is shared by all such calls on a device:
+ *     it is correct across host threads but serialises their cold-segment
+ *     kernels, and a capture on one thread must not overlap a bf16 prefill
+ *     forward on another thread of the same device.
+ *     moe_experts_forward_noalloc keeps everything on `stream`.
  *   - Inputs are read-only; outputs are overwritten.
  *   - Calls with distinct workspaces may run concurrently. Two calls in flight
  *     on one workspace race.

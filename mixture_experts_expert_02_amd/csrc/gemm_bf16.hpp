@@ -319,48 +319,54 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int mt, int nt, int s
         __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA[(k) >> 1], dB[(k) & 1], acc[(k) >> 1][(k) & 1], 0, 0, 0); \
   }
   // one k-substep: MFMAs on (cA, cB), each followed by one read of the next
-  // substep's fragments (nA, nB from stage buffer nst, substep nks) and, in
-  // the first substep of a stage with a next stage, one of this wave's four
-  // loads of it
-#define MOE_W16_SUBSTEP(cA, cB, nA, nB, nst, nks, dma)                       \
+  // substep's fragments (nA, nB from stage buffer nst, substep nks)
+#define MOE_W16_SUBSTEP(cA, cB, nA, nB, nst, nks)                            \
   {                                                                           \
     MOE_W16_WAIT_TIE(cA, cB);                                                 \
     _Pragma("unroll") for (int k = 0; k < 4; ++k) {                           \
-      if (dma) MOE_W16_DMA(stn, kl, k)                                        \
       MOE_W16_READ1(nA, nB, nst, nks, k)                                      \
       MOE_W16_MFMA(cA, cB, k)                                                 \
       __builtin_amdgcn_sched_barrier(0);                                      \
     }                                                                         \
   }
 
-  // prologue: stage 0
+  // prologue: stages 0 and 1 (one into each buffer); stage 0 is read first
 #pragma unroll
   for (int q = 0; q < 4; ++q) MOE_W16_DMA(0, 0u, q)
+  if (KT > 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) MOE_W16_DMA(1, (uint32_t)(BK * 2), q)
+  }
   wait_vmcnt<0>();
   stage_barrier();
 #pragma unroll
   for (int q = 0; q < 4; ++q) MOE_W16_READ1(fa, fb, 0, 0, q)
 
-  // Stage s (buffer st = s & 1): its first substep issues the loads of stage
-  // s + 1 into the other buffer (which every wave finished reading before the
-  // last barrier). In the last substep, after the first MFMA, a wave waits
-  // for its loads of stage s + 1 and meets the others at the barrier; the
-  // reads of stage s + 1's first fragments go with the remaining MFMAs.
+  // Stage s (buffer st = s & 1), with stage s + 1 loading into the other
+  // buffer. In the last substep, after the first MFMA, a wave waits for its
+  // loads of stage s + 1 and meets the others at the barrier. Past that
+  // barrier every wave has read its last fragments of stage s, so the loads
+  // of stage s + 2 go into this stage's buffer at once, one with each of the
+  // remaining MFMAs, along with the reads of stage s + 1's first fragments:
+  // the load path, which bounds the kernel, has work again as soon as a
+  // stage's loads are in.
 #define MOE_W16_STAGE(LOAD)                                      \
   {                                                              \
     const int stn = st ^ 1;                                      \
-    const uint32_t kl = (uint32_t)(s + 1) * BK * 2u;             \
-    MOE_W16_SUBSTEP(fa, fb, ga, gb, st, 1, LOAD)                 \
-    MOE_W16_SUBSTEP(ga, gb, fa, fb, st, 2, false)                \
-    MOE_W16_SUBSTEP(fa, fb, ga, gb, st, 3, false)                \
+    const uint32_t kl2 = (uint32_t)(s + 2) * BK * 2u;            \
+    const bool issue2 = LOAD && s + 2 < KT;                      \
+    MOE_W16_SUBSTEP(fa, fb, ga, gb, st, 1)                       \
+    MOE_W16_SUBSTEP(ga, gb, fa, fb, st, 2)                       \
+    MOE_W16_SUBSTEP(fa, fb, ga, gb, st, 3)                       \
     MOE_W16_WAIT_TIE(ga, gb);                                    \
     _Pragma("unroll") for (int k = 0; k < 4; ++k) {              \
       MOE_W16_MFMA(ga, gb, k)                                    \
       __builtin_amdgcn_sched_barrier(0);                         \
       if (LOAD && k == 0) {                                      \
-        wait_vmcnt<0>();                                    \
-        stage_barrier();                                    \
+        wait_vmcnt<0>();                                         \
+        stage_barrier();                                         \
       }                                                          \
+      if (issue2) MOE_W16_DMA(st, kl2, k)                        \
       if (LOAD) MOE_W16_READ1(fa, fb, stn, 0, k)                 \
     }                                                            \
     st = stn;                                                    \

@@ -22,13 +22,12 @@
 // through two 64 KB stages: the loads of stage s+1 run under the MFMAs of
 // stage s. Wave w fills rows 16 w..16 w+15 of a stage's A and of its B
 // (GEMM1: waves 0-7 gate rows, 8-15 up rows), two 8-row instructions each.
-// Sixteen waves rather than eight with 128 x 64 blocks: a compute unit's
-// rate for these loads grows with the number of waves issuing them when the
-// lines hit in L2 (about 27 bytes a clock with 8 waves and 43 with 16 in a
-// streaming probe; a stage needs 64 KB per 2048 MFMA cycles, 32 bytes a
-// clock), and four waves per SIMD hide the operand reads better (the loop
-// without its loads runs about 7% faster than with eight waves). With the L2
-// misses of these grouped shapes the load path still bounds the kernel.
+// Sixteen waves rather than eight with 128 x 64 blocks: eight waves read a
+// quarter fewer operand bytes from LDS per MFMA, but with two waves per SIMD
+// the operand reads and barriers are hidden worse, and the whole kernel
+// measured the same or slightly slower. A stage needs 64 KB per 2048 MFMA
+// cycles (32 bytes a clock); with the L2 misses of these grouped shapes the
+// load path bounds the kernel.
 // Only vmcnt(0) reliably orders the completion of these direct-to-LDS
 // loads, so a wave waits for all of its loads before each stage barrier. The
 // 16-byte chunks of every row are XOR-swizzled so that the MFMA operand

@@ -335,13 +335,37 @@ __device__ __forceinline__ uint32_t gather4(uint32_t b) {
          ((uint32_t)__shfl_down((int)b, 2) & 0xffu) << 16 | ((uint32_t)__shfl_down((int)b, 3) & 0xffu) << 24;
 }
 
-// LDS of one decode tile: two activation buffers, the per-wave weight
-// rearrangement region (MXFP4), the block maxima exchanged by wave pairs.
+// 4 x 4 transpose between a lane's four registers and lane bits 2-3: lane
+// l of register j receives what lane l' of register j' held, where l' is l
+// with bits 2-3 replaced by j and j' is bits 2-3 of l. Two butterfly stages
+// (bit 2 with register bit 0, then bit 3 with register bit 1); each moves
+// data 4 or 8 lanes within a 16-lane row (DPP row shifts) and selects.
+template <int BIT>
+__device__ __forceinline__ void quad_swap(u32x4& a, u32x4& b, bool hi) {
+  constexpr int SHR = 0x110 + BIT, SHL = 0x100 + BIT;  // DPP row_shr:BIT, row_shl:BIT
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t from_b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b[d], SHR, 0xf, 0xf, false);
+    const uint32_t from_a = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a[d], SHL, 0xf, 0xf, false);
+    const uint32_t na = hi ? from_b : a[d];
+    const uint32_t nb = hi ? b[d] : from_a;
+    a[d] = na;
+    b[d] = nb;
+  }
+}
+__device__ __forceinline__ void quad_transpose(u32x4 (&r)[4], int lane) {
+  const bool b2 = (lane & 4) != 0, b3 = (lane & 8) != 0;
+  quad_swap<4>(r[0], r[1], b2);
+  quad_swap<4>(r[2], r[3], b2);
+  quad_swap<8>(r[0], r[2], b3);
+  quad_swap<8>(r[1], r[3], b3);
+}
+
+// LDS of one decode tile: two activation buffers, the block maxima
+// exchanged by wave pairs.
 template <int FMT>
 struct TileLds {
-  static constexpr int kWtStep = 16 * 64 + 16;
   __attribute__((aligned(16))) uint8_t sbuf[2][Cfg<FMT>::BUF_BYTES];
-  __attribute__((aligned(16))) uint8_t wtr[FMT == W_MXFP4 ? NW : 1][FMT == W_MXFP4 ? 8 * kWtStep : 16];
   float half_amax[NW][BM];
 };
 
@@ -358,9 +382,7 @@ template <int FMT, bool GATED, int SPT, bool A8, bool FUSED>
 __device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, TileLds<FMT>& L,
                                             const FusedSync& fs) {
   using C = Cfg<FMT>;
-  constexpr int kWtStep = TileLds<FMT>::kWtStep;
   auto& sbuf = L.sbuf;
-  auto& wtr = L.wtr;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (mt >= __builtin_amdgcn_readfirstlane(p.status[2])) return;  // workgroup-uniform, before any barrier
@@ -385,16 +407,20 @@ __device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, Til
       weight_rsrc((const uint8_t*)(GATED ? p.B1 : p.B0) + (size_t)seg * segbytes, segbytes);
   constexpr uint32_t BLOCK_BYTES = FMT == W_MXFP4 ? 16 : 64;
   // bf16: lane (l16, q) loads its own blocks. MXFP4: a chunk is 256 bytes of
-  // each of a stream's 16 rows, loaded as 4 rows x 256 bytes per instruction
-  // (instruction j: row 4 j + q, bytes 16 l16), whole 128-byte lines per
-  // request, and rearranged through LDS into the MFMA operand layout.
+  // each of a stream's 16 rows, loaded as 4 rows x 256 bytes per instruction,
+  // whole 128-byte lines per request: instruction j, lane (l16, q) reads row
+  // 4 j + (l16 % 4), 16-byte block 4 (l16 / 4) + q. quad_transpose then
+  // exchanges the instruction index with lane bits 2-3, which leaves register
+  // u holding, in lane (l16, q), block 4 u + q of row l16: the MFMA operand
+  // of step u.
   uint32_t vo0[FMT == W_MXFP4 ? 4 : 1], vo1[FMT == W_MXFP4 ? 4 : 1];
+  const int piece = 4 * (l16 >> 2) + q;  // MXFP4: this lane's 16-byte block of a chunk's 256 bytes
   if (FMT == W_MXFP4) {
     const int b1 = GATED ? nb : nb + 16;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      vo0[j] = (uint32_t)min(nb + 4 * j + q, N - 1) * rowbytes + 16 * l16;
-      vo1[j] = (uint32_t)min(b1 + 4 * j + q, N - 1) * rowbytes + 16 * l16;
+      vo0[j] = (uint32_t)min(nb + 4 * j + (l16 & 3), N - 1) * rowbytes + 16 * piece;
+      vo1[j] = (uint32_t)min(b1 + 4 * j + (l16 & 3), N - 1) * rowbytes + 16 * piece;
     }
   } else {
     vo0[0] = (uint32_t)min(c0, N - 1) * rowbytes + BLOCK_BYTES * q;
@@ -507,10 +533,10 @@ __device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, Til
   // next row's bytes would only meet zero activations.
   auto load_chunk = [&](WSet<FMT>& w, int c) {
     const int so = c < nch ? c * C::SPC * 4 * BLOCK_BYTES : (int)segbytes;
-    const bool in_row = (uint32_t)so + 16u * l16 < rowbytes;
+    const bool in_row = (uint32_t)so + 16u * (FMT == W_MXFP4 ? piece : l16) < rowbytes;
 #pragma unroll
     for (int u = 0; u < C::SPC; ++u) {
-      if (FMT == W_MXFP4) {  // w.w0[u]: instruction u (rows 4 u + q)
+      if (FMT == W_MXFP4) {  // w.w0[u]: instruction u (rows 4 u + l16 % 4)
         w.w0[u].q[0] = __builtin_amdgcn_raw_buffer_load_b128(rs0, in_row ? vo0[u] : segbytes, so, 0);
         w.w1[u].q[0] = __builtin_amdgcn_raw_buffer_load_b128(rs1, in_row ? vo1[u] : segbytes, so, 0);
       } else {
@@ -528,17 +554,12 @@ __device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, Til
   auto compute = [&](const WSet<FMT>& w, int buf, int c) {
     if (!wave_on) return;
     if constexpr (QA) {
-      // rearrange: lane (l16, q) of instruction j holds row 4 j + q, block
-      // l16 of the chunk = step l16 / 4, lane group l16 % 4; the wave's
-      // region is [stream][step][row][group] x 16 bytes, steps padded by 16
-      // bytes against bank conflicts
-      uint8_t* wt = &wtr[wave][0];
-#pragma unroll
-      for (int j = 0; j < C::SPC; ++j) {
-        const int o = (l16 >> 2) * kWtStep + (4 * j + q) * 64 + (l16 & 3) * 16;
-        *(u32x4*)(wt + o) = w.w0[j].q[0];
-        *(u32x4*)(wt + 4 * kWtStep + o) = w.w1[j].q[0];
-      }
+      // the weights of each stream in the MFMA operand layout, one register
+      // per step (see quad_transpose)
+      u32x4 t0[4] = {w.w0[0].q[0], w.w0[1].q[0], w.w0[2].q[0], w.w0[3].q[0]};
+      u32x4 t1[4] = {w.w1[0].q[0], w.w1[1].q[0], w.w1[2].q[0], w.w1[3].q[0]};
+      quad_transpose(t0, lane);
+      quad_transpose(t1, lane);
       const uint8_t* hrow = &sbuf[buf][l16 * C::QROW];
       const uint8_t* lrow = hrow + BM * C::QROW;
       const uint8_t* srow = &sbuf[buf][2 * BM * C::QROW + 16 * l16];
@@ -556,8 +577,8 @@ __device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, Til
         const i32x8 al = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3], (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
         const int sa = srow[4 * u + q];
         const int sb0 = sc0[kbc], sb1 = sc1[kbc];
-        const u32x4 c0w = *(const u32x4*)(wt + u * kWtStep + l16 * 64 + q * 16);
-        const u32x4 c1w = *(const u32x4*)(wt + (4 + u) * kWtStep + l16 * 64 + q * 16);
+        const u32x4 c0w = t0[u];
+        const u32x4 c1w = t1[u];
         const i32x8 b0 = {(int)c0w[0], (int)c0w[1], (int)c0w[2], (int)c0w[3], 0, 0, 0, 0};
         const i32x8 b1 = {(int)c1w[0], (int)c1w[1], (int)c1w[2], (int)c1w[3], 0, 0, 0, 0};
         acc0 = mfma_fp8_fp4(ah, b0, acc0, sa, sb0);

@@ -68,6 +68,9 @@ def parse():
                          "default: the workload's own")
     ap.add_argument("--weight-copies", type=int, default=4,
                     help="MXFP4 decode: copies of the weights the steps rotate over")
+    ap.add_argument("--row-layout", action="store_true",
+                    help="bf16 workloads: keep the weights in their row layout instead of the operand-block "
+                         "layout made once before the timed steps (moe_bf16_pack_weights)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -280,6 +283,13 @@ def run_pregrouped(args, wl, dev, K):
     rw = synth.make_route_weights_nvs(wl)
     cu_d, rw_d = torch.from_numpy(cu).to(dev), torch.from_numpy(rw).to(dev)
     p = B.problem(wl.T, wl.H, wl.I, wl.E, 1, wl.wfmt, wl.act, wl.alpha, wl.beta, wl.limit)
+    packed = None
+    if wl.wfmt == "bf16" and not args.row_layout:
+        # the prefill kernels' operand-block weight layout, made once before the
+        # timed steps (flashinfer_moe_ep page, process_weights_after_loading)
+        packed = B.bf16_pack_weights(p, *W)
+        torch.cuda.synchronize()
+        p.bf16_packed = packed.data_ptr()
     ws = B.alloc_workspace(B.moe_experts_grouped_workspace_bytes(p), dev)
     out = torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
@@ -314,7 +324,9 @@ def run_pregrouped(args, wl, dev, K):
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "steps": K,
         "ms_per_step": round(ms_per_step, 4), "dtype": "bf16",
         "config": {"workload": wl.name, "NvS": wl.T, "H": wl.H, "I": wl.I, "segments": wl.E, "weights": wl.wfmt,
-                   "activation": wl.act, "routed_rows": M, "touched_experts": n_touched},
+                   "activation": wl.act, "routed_rows": M, "touched_experts": n_touched,
+                   **({"weight_layout": "packed once before the timed steps (moe_bf16_pack_weights)"}
+                      if packed is not None else {})},
         "stage_ms": {s: round(v, 4) for s, v in avg.items()},
         "event_ms_per_step": round(step_ms, 4),
         "instrumented_ms_per_step": round(instr_ms, 4),
@@ -355,6 +367,11 @@ def run_token_major(args, wl, dev, K, act_fmt):
         packed = B.mx_pack_weights(p, *W, *S)
         torch.cuda.synchronize()
         p.mx_packed = packed.data_ptr()
+    elif wl.wfmt == "bf16" and not args.row_layout:
+        # the bf16 prefill kernels' operand-block layout, made the same way
+        packed = B.bf16_pack_weights(p, *W)
+        torch.cuda.synchronize()
+        p.bf16_packed = packed.data_ptr()
     ws = B.alloc_workspace(B.moe_experts_workspace_bytes(p), dev)
     out = torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
@@ -449,7 +466,9 @@ def run_token_major(args, wl, dev, K, act_fmt):
                    "weights": wl.wfmt, "activation": wl.act, "routed_rows": M, "touched_experts": n_touched,
                    **({"weight_copies": copies} if copies > 1 else {}),
                    **({"activations": act_fmt} if act_fmt != "bf16" else {}),
-                   **({"weight_layout": "packed once (moe_mx_pack_weights)"} if packed is not None else {})},
+                   **({"weight_layout": "packed once before the timed steps ("
+                                        + ("moe_mx_pack_weights)" if wl.wfmt == "mxfp4" else "moe_bf16_pack_weights)")}
+                      if packed is not None else {})},
         "stage_ms": {s: round(v, 4) for s, v in avg.items()},
         "event_ms_per_step": round(float(np.mean(step_ms)), 4),
         "instrumented_ms_per_step": round(instr_ms, 4),

@@ -149,6 +149,18 @@ typedef struct {
    * stale packing from a fresh one: re-pack after changing the weights. Set
    * with any other weight or activation format: MOE_EINVAL. */
   const void* mx_packed;
+  /* bf16 weights: the same weights in the operand-block layout, written by
+   * moe_bf16_pack_weights (device, 16-byte aligned), or NULL (the
+   * zero-initialised default). flashinfer_moe_ep page,
+   * process_weights_after_loading: the weights are put into the kernel's
+   * format once, before the first forward. When set, the tiled and the
+   * cold-segment prefill kernels (both entries) read the weights from here:
+   * each 1 KB load is then one contiguous block in MFMA operand order; the
+   * results are bitwise those of the row layout. The canonical tensors are
+   * still required (the weight-streaming kernels of small problems read
+   * them). Re-pack after changing the weights. Set with another weight
+   * format: MOE_EINVAL. */
+  const void* bf16_packed;
 } moe_problem;
 
 /* Byte offsets of the intermediates inside a forward workspace (for tests and
@@ -220,6 +232,25 @@ size_t moe_mx_packed_bytes(const moe_problem* p);
 int moe_mx_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up, const void* w_down,
                         const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down, void* packed,
                         size_t packed_bytes, moe_stream_t stream);
+
+/* Bytes of the bf16 operand-block weights (moe_problem.bf16_packed) of problem
+ * p: the gate weights [E, I, H], then the up weights [E, I, H], then the down
+ * weights [E, H, I], 2 E I H bytes each, each matrix [N, K] stored as 1 KB
+ * blocks of 16 rows x 32 K values, block (nb, kb) at ((e N / 16 + nb) K / 32 +
+ * kb) * 1024 bytes from its region's start, its 16-byte piece l (l < 64)
+ * holding row 16 nb + l % 16, values 32 kb + 8 (l / 16)..+7 (the B operand of
+ * v_mfma_f32_16x16x32_bf16, lane by lane). 0 when p is invalid or its weights
+ * are not bf16. flashinfer_moe_ep page, process_weights_after_loading. */
+size_t moe_bf16_packed_bytes(const moe_problem* p);
+
+/* Writes the operand-block weights of problem p (moe_bf16_packed_bytes bytes)
+ * into packed (device, 16-byte aligned, caller-owned) from the canonical bf16
+ * tensors w_gate, w_up [E, I, H] and w_down [E, H, I] (device, 16-byte
+ * aligned), on stream; asynchronous like the forward. Host-side errors before
+ * any launch: MOE_EINVAL (invalid p, weights not bf16, a NULL or misaligned
+ * pointer), MOE_ENOSPC (packed_bytes below moe_bf16_packed_bytes). */
+int moe_bf16_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up, const void* w_down,
+                          void* packed, size_t packed_bytes, moe_stream_t stream);
 
 /* Workspace bytes a moe_experts_forward call on problem *p needs (0 if *p is
  * invalid). Depends only on the sizes in *p, so a workspace sized once for the

@@ -30,7 +30,8 @@ EXPORTED = (
     "moe_experts_forward_timed", "moe_align_workspace_bytes", "moe_align",
     "moe_experts_grouped_workspace_bytes", "moe_experts_forward_grouped", "moe_device_error",
     "moe_strerror", "moe_route", "moe_experts_forward_grouped_timed", "moe_experts_forward_noalloc",
-    "moe_check_expert_params", "moe_mx_packed_bytes", "moe_mx_pack_weights",
+    "moe_check_expert_params", "moe_mx_packed_bytes", "moe_mx_pack_weights", "moe_bf16_packed_bytes",
+    "moe_bf16_pack_weights",
 )
 MOE_ROUTE_RENORMALIZE, MOE_ROUTE_DEEPSEEK_V3 = 0, 1
 _ROUTE = {"renormalize": MOE_ROUTE_RENORMALIZE, "deepseek_v3": MOE_ROUTE_DEEPSEEK_V3}
@@ -42,7 +43,8 @@ class MoeProblem(ctypes.Structure):
                 ("act", ctypes.c_int32), ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
                 ("limit", ctypes.c_float), ("weight_on_input", ctypes.c_int32), ("a_fmt", ctypes.c_int32),
                 ("alpha_e", ctypes.c_void_p), ("beta_e", ctypes.c_void_p), ("limit_e", ctypes.c_void_p),
-                ("fc1_alpha", ctypes.c_void_p), ("fc2_alpha", ctypes.c_void_p), ("mx_packed", ctypes.c_void_p)]
+                ("fc1_alpha", ctypes.c_void_p), ("fc2_alpha", ctypes.c_void_p), ("mx_packed", ctypes.c_void_p),
+                ("bf16_packed", ctypes.c_void_p)]
 
 
 class MoeRouteProblem(ctypes.Structure):
@@ -108,6 +110,10 @@ def lib() -> ctypes.CDLL:
         L.moe_mx_packed_bytes.restype = sz
         L.moe_mx_pack_weights.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_mx_pack_weights.restype = ctypes.c_int
+        L.moe_bf16_packed_bytes.argtypes = [P]
+        L.moe_bf16_packed_bytes.restype = sz
+        L.moe_bf16_pack_weights.argtypes = [P, vp, vp, vp, vp, sz, vp]
+        L.moe_bf16_pack_weights.restype = ctypes.c_int
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -197,6 +203,25 @@ def mx_pack_weights(p: MoeProblem, w_gate, w_up, w_down, s_gate, s_up, s_down, s
     return packed
 
 
+def moe_bf16_packed_bytes(p: MoeProblem) -> int:
+    return lib().moe_bf16_packed_bytes(ctypes.byref(p))
+
+
+def moe_bf16_pack_weights(p: MoeProblem, w_gate, w_up, w_down, packed, stream=None) -> int:
+    return lib().moe_bf16_pack_weights(ctypes.byref(p), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(packed),
+                                       packed.numel() * packed.element_size(), _stream(stream))
+
+
+def bf16_pack_weights(p: MoeProblem, w_gate, w_up, w_down, stream=None) -> torch.Tensor:
+    """Operand-block weights of problem p (a new uint8 device tensor); set p.bf16_packed to its pointer."""
+    n = moe_bf16_packed_bytes(p)
+    if n == 0:
+        raise MoeError(MOE_EINVAL, "moe_bf16_packed_bytes")
+    packed = torch.empty(n, dtype=torch.uint8, device=w_gate.device)
+    _check(moe_bf16_pack_weights(p, w_gate, w_up, w_down, packed, stream=stream), "moe_bf16_pack_weights")
+    return packed
+
+
 def moe_experts_forward(p: MoeProblem, x, topk_ids, topk_weights, w_gate, w_up, w_down, s_gate, s_up, s_down,
                         out, workspace, stream=None) -> int:
     return lib().moe_experts_forward(ctypes.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w_gate),
@@ -276,9 +301,10 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
 
 def experts_forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, scales=None, act="silu", alpha=1.0, beta=0.0,
                     limit=math.inf, out=None, workspace=None, weight_on_input=False,
-                    act_fmt="bf16", expert_params=None, mx_packed=None) -> torch.Tensor:
+                    act_fmt="bf16", expert_params=None, mx_packed=None, bf16_packed=None) -> torch.Tensor:
     """Token-major experts step on torch tensors; allocates out/workspace if not given.
-    mx_packed: the weights packed by mx_pack_weights (MXFP4 x MXFP8 only), or None."""
+    mx_packed: the weights packed by mx_pack_weights (MXFP4 x MXFP8 only), or None.
+    bf16_packed: the weights packed by bf16_pack_weights (bf16 only), or None."""
     T, H = x.shape
     k = topk_ids.shape[1]
     E = w_gate.shape[0]
@@ -287,6 +313,8 @@ def experts_forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, scales=None
     p = problem(T, H, I, E, k, wfmt, act, alpha, beta, limit, weight_on_input, act_fmt, expert_params)
     if mx_packed is not None:
         p.mx_packed = mx_packed.data_ptr()
+    if bf16_packed is not None:
+        p.bf16_packed = bf16_packed.data_ptr()
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
     if workspace is None:
@@ -299,12 +327,15 @@ def experts_forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, scales=None
 
 def experts_forward_grouped(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, scales=None, act="silu", alpha=1.0,
                             beta=0.0, limit=math.inf, out=None, workspace=None, weight_on_input=False,
-                            act_fmt="bf16", expert_params=None) -> torch.Tensor:
+                            act_fmt="bf16", expert_params=None, bf16_packed=None) -> torch.Tensor:
+    """Pre-grouped experts step; bf16_packed: the weights packed by bf16_pack_weights (bf16 only), or None."""
     NvS, H = x_nvs.shape
     G = w_gate.shape[0]
     I = w_gate.shape[1]
     wfmt = "mxfp4" if w_gate.dtype == torch.uint8 else "bf16"
     p = problem(NvS, H, I, G, 1, wfmt, act, alpha, beta, limit, weight_on_input, act_fmt, expert_params)
+    if bf16_packed is not None:
+        p.bf16_packed = bf16_packed.data_ptr()
     if out is None:
         out = torch.empty(NvS, H, dtype=torch.bfloat16, device=x_nvs.device)
     if workspace is None:

@@ -28,6 +28,12 @@
 // measured the same or slightly slower. A stage needs 64 KB per 2048 MFMA
 // cycles (32 bytes a clock); with the L2 misses of these grouped shapes the
 // load path bounds the kernel.
+// Weights in the operand-block layout (PK, written once by k_bf16_pack): each
+// 16-row x 32-K block of an expert's [N, K] matrix is 1 KB in
+// v_mfma_f32_16x16x32_bf16 operand order, so a wave's B instruction copies
+// one contiguous block (its 16 rows, half of the stage's K) and the B
+// fragments are read from that order instead of the swizzled rows; the
+// arithmetic and its order are those of the row layout.
 // Only vmcnt(0) reliably orders the completion of these direct-to-LDS
 // loads, so a wave waits for all of its loads before each stage barrier. The
 // 16-byte chunks of every row are XOR-swizzled so that the MFMA operand
@@ -83,6 +89,35 @@ struct Params {
 // distinct 16-byte banks.
 __device__ __forceinline__ int lds_slot(int row, int chunk) {
   return row * (BK / 8) + (chunk ^ ((row >> 1) & 7));
+}
+
+// Operand-block layout of a [G, N, K] bf16 weight (N a multiple of 16, K of
+// 32): block (g, nb, kb) of 16 rows x 32 K values is 1 KB at byte
+// ((g * N / 16 + nb) * K / 32 + kb) * 1024, and its 16-byte piece l (l < 64)
+// holds row 16 nb + l % 16, values 32 kb + 8 (l / 16)..+7: the B operand of
+// v_mfma_f32_16x16x32_bf16 for those rows and K values, lane by lane. Same
+// size as the row layout. In a stage of the tile kernel, B block (w, h) (w =
+// 16-row block of the tile, h = K half) lands at B_HALF + (2 w + h) * 1024,
+// so a tile row R and 16-byte K chunk c of the stage sit at
+// B_HALF + ((R / 16) * 2 + c / 4) * 1024 + (R % 16 + 16 (c % 4)) * 16: rows 32
+// apart are 4096 bytes apart, as in the row layout.
+__device__ __forceinline__ uint32_t pk_lds_off(int row, int chunk) {
+  return (uint32_t)((((row >> 4) * 2 + (chunk >> 2)) * 1024) + ((row & 15) + 16 * (chunk & 3)) * 16);
+}
+
+// Writes a [G, N, K] bf16 weight in the operand-block layout (one 16-byte
+// piece per thread and step, grid-stride; pieces = G N K / 8).
+__global__ __launch_bounds__(256) void k_bf16_pack(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                   int N, int K, long long pieces) {
+  const long long nkb = K / 32, nnb = N / 16;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < pieces; i += (long long)gridDim.x * 256) {
+    const long long b = i >> 6;
+    const int l = (int)(i & 63);
+    const long long kb = b % nkb, t = b / nkb;
+    const long long nb = t % nnb, g = t / nnb;
+    const long long row = g * N + nb * 16 + (l & 15), col = kb * 32 + 8 * (l >> 4);
+    *(u32x4*)(dst + i * 8) = *(const u32x4*)(src + row * K + col);
+  }
 }
 
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -217,7 +252,7 @@ __device__ __forceinline__ void item_tile(const P& p, int item, int mtl, int nsp
   }
 }
 
-template <bool GATED, int AK>
+template <bool GATED, int AK, bool PK>
 __device__ __forceinline__ void gemm_tile(const Params& p, int mt, int nt, int split, int nsplit, lds_u8* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -250,8 +285,13 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int mt, int nt, int s
       int arow = first;
       if (r < rows) arow = p.a_perm ? p.a_perm[row0 + r] / p.a_div : row0 + r;
       a_off[q] = ((uint32_t)arow * (uint32_t)K + chunk * 8) * 2u + kb0;
-      const int n = min(n0 + (GATED ? (r & 127) : r), N - 1);
-      b_off[q] = ((uint32_t)n * (uint32_t)K + chunk * 8) * 2u + kb0;
+      if constexpr (PK) {  // the wave's 16 rows are one block row; instruction q = K half q of the stage
+        const int nb = min((n0 >> 4) + (GATED ? (wave & 7) : wave), N / 16 - 1);
+        b_off[q] = ((uint32_t)nb * (uint32_t)(K / 32) + 2u * (uint32_t)st_lo + (uint32_t)q) * 1024u + (uint32_t)lane * 16u;
+      } else {
+        const int n = min(n0 + (GATED ? (r & 127) : r), N - 1);
+        b_off[q] = ((uint32_t)n * (uint32_t)K + chunk * 8) * 2u + kb0;
+      }
     }
   }
   // 8-row blocks of A past the segment end are not loaded (their rows of the
@@ -265,7 +305,7 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int mt, int nt, int s
       if ((q) == 0 ? a_live0 : a_live1)                                                                 \
         __builtin_amdgcn_global_load_lds(Ab + (a_off[(q) & 1] + (kbytes)), (__attribute__((address_space(3))) void*)dst_, 16, 0, 0); \
     } else {                                                                                            \
-      __builtin_amdgcn_global_load_lds(Bw + (b_off[(q) & 1] + (kbytes)),                                \
+      __builtin_amdgcn_global_load_lds(Bw + (b_off[(q) & 1] + (kbytes) * (PK ? 16u : 1u)),              \
                                        (__attribute__((address_space(3))) void*)(dst_ + B_HALF), 16, 0, 0); \
     }                                                                                                   \
   }
@@ -281,7 +321,9 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int mt, int nt, int s
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     a_lane[ks] = lds0 + 16u * lds_slot(wm * 64 + lr, ks * 2 + lk);
-    b_lane[ks] = lds0 + B_HALF + 16u * lds_slot((GATED ? wn * 32 : wn * 64) + lr, ks * 2 + lk);
+    b_lane[ks] = lds0 + B_HALF +
+                 (PK ? pk_lds_off((GATED ? wn * 32 : wn * 64) + lr, ks * 2 + lk)
+                     : 16u * lds_slot((GATED ? wn * 32 : wn * 64) + lr, ks * 2 + lk));
   }
 
   f32x16 acc[2][2];
@@ -397,7 +439,7 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int mt, int nt, int s
 // item_tile); the hardware sends workgroup b to XCD b mod 8,
 // and each XCD takes a contiguous run of items, so tiles that share weight
 // and row panels share an L2. Blocks past the last item exit.
-template <bool GATED, int AK>
+template <bool GATED, int AK, bool PK>
 __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_num_vgpr(96))) void k_gemm(const Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem_arr[NS * STAGE_BYTES];
   const int mtl = p.status[2];
@@ -411,7 +453,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_num_vgpr(96))) void k_
   if (item >= n_live) return;
   int mt, nt, split;
   item_tile(p, item, mtl, nsplit, mt, nt, split);
-  gemm_tile<GATED, AK>(p, mt, nt, split, nsplit, (lds_u8*)smem_arr);
+  gemm_tile<GATED, AK, PK>(p, mt, nt, split, nsplit, (lds_u8*)smem_arr);
 }
 
 }  // namespace big

@@ -28,7 +28,11 @@
 // 4 (l / 16)..4 (l / 16)+3. The weights go from memory into registers two
 // steps ahead (16 lanes read 64 contiguous bytes of each of 16 rows, the next
 // step the rest of those 128-byte lines); the rows are staged through LDS 64 K
-// at a time (double-buffered), loaded one chunk ahead.
+// at a time (double-buffered), loaded one chunk ahead. With the weights in
+// the operand-block layout (PK; the layout is defined beside the tile kernel)
+// a step's 16 rows are one contiguous 1 KB block already in operand order,
+// lane l's 16 bytes at 16 l: whole lines, consecutive lanes on consecutive
+// bytes.
 #pragma once
 
 #include "common.hpp"
@@ -65,7 +69,7 @@ struct Params {
   ExpertParams ep;
 };
 
-template <bool GATED, int AK>
+template <bool GATED, int AK, bool PK>
 __global__ __launch_bounds__(NT, 8) void k_cold(const Params p) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[2][MAX_ROWS * LROW];
   const int tid = threadIdx.x;
@@ -82,12 +86,24 @@ __global__ __launch_bounds__(NT, 8) void k_cold(const Params p) {
     const int rows = p.seg_end[seg] - row0;  // 1 .. MAX_ROWS
     const bool two = rows > 16;
 
-    // this lane's weight rows (rows past N read row N - 1; never stored)
+    // this lane's weight rows (rows past N read row N - 1, or the last
+    // 16-row block; never stored); a lane's operand of 32-K step s is at
+    // b0 + s * SSTEP (and b1 + s * SSTEP)
     const int c0 = GATED ? nt * 64 + wave * 16 : nt * 128 + wave * 32;
     const size_t wbase = (size_t)seg * N * K;
-    const uint16_t* b0 = p.B0 + wbase + (size_t)min(c0 + l16, N - 1) * K + 8 * q;
-    const uint16_t* b1 = (GATED ? p.B1 + wbase + (size_t)min(c0 + l16, N - 1) * K
-                                : p.B0 + wbase + (size_t)min(c0 + 16 + l16, N - 1) * K) + 8 * q;
+    constexpr int SSTEP = PK ? 512 : 32;
+    const uint16_t* b0;
+    const uint16_t* b1;
+    if constexpr (PK) {
+      const size_t brow = (size_t)(K / 32) * 512;  // elements of a 16-row block row
+      const int nb0 = min(c0 >> 4, N / 16 - 1), nb1 = min((c0 >> 4) + 1, N / 16 - 1);
+      b0 = p.B0 + wbase + nb0 * brow + 8 * lane;
+      b1 = (GATED ? p.B1 + wbase + nb0 * brow : p.B0 + wbase + nb1 * brow) + 8 * lane;
+    } else {
+      b0 = p.B0 + wbase + (size_t)min(c0 + l16, N - 1) * K + 8 * q;
+      b1 = (GATED ? p.B1 + wbase + (size_t)min(c0 + l16, N - 1) * K
+                  : p.B0 + wbase + (size_t)min(c0 + 16 + l16, N - 1) * K) + 8 * q;
+    }
     // this thread's 16-byte piece of a staged chunk (32 rows x 64 K): row
     // tid / 8, K values 8 (tid % 8)..; rows past the segment end read its last
     // row
@@ -104,8 +120,8 @@ __global__ __launch_bounds__(NT, 8) void k_cold(const Params p) {
     u32x4 wb[2][2];  // weights of two steps: [step & 1][stream]
     wb[0][0] = *(const u32x4*)b0;
     wb[0][1] = *(const u32x4*)b1;
-    wb[1][0] = *(const u32x4*)(b0 + 32);
-    wb[1][1] = *(const u32x4*)(b1 + 32);
+    wb[1][0] = *(const u32x4*)(b0 + SSTEP);
+    wb[1][1] = *(const u32x4*)(b1 + SSTEP);
     __syncthreads();
 
     f32x4 acc[2][2];
@@ -131,8 +147,8 @@ __global__ __launch_bounds__(NT, 8) void k_cold(const Params p) {
           acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bv1, acc[1][1], 0, 0, 0);
         }
         if (s + 2 < 2 * nch) {
-          wb[j][0] = *(const u32x4*)(b0 + (s + 2) * 32);
-          wb[j][1] = *(const u32x4*)(b1 + (s + 2) * 32);
+          wb[j][0] = *(const u32x4*)(b0 + (s + 2) * SSTEP);
+          wb[j][1] = *(const u32x4*)(b1 + (s + 2) * SSTEP);
         }
       }
       if (more) *(u32x4*)&sa[(c + 1) & 1][sl] = ar;

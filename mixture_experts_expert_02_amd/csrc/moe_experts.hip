@@ -140,6 +140,7 @@ int check_problem(const moe_problem* p, bool grouped) {
   if (p->a_fmt == MOE_A_MXFP8 && p->wfmt != MOE_W_MXFP4) return MOE_ENOTSUP;  // block-scaled MFMA path only
   if (p->mx_packed && (p->wfmt != MOE_W_MXFP4 || p->a_fmt != MOE_A_MXFP8 || !aligned16(p->mx_packed)))
     return MOE_EINVAL;
+  if (p->bf16_packed && (p->wfmt != MOE_W_BF16 || !aligned16(p->bf16_packed))) return MOE_EINVAL;
   const void* ep[] = {p->alpha_e, p->beta_e, p->limit_e, p->fc1_alpha, p->fc2_alpha};
   for (const void* q : ep)
     if (((uintptr_t)q & 3u) != 0) return MOE_EINVAL;
@@ -477,6 +478,44 @@ struct GemmIO {
   moe::skinny::QRows Cq;  // GEMM1 with MXFP8 activations: C quantized instead of written as bf16
 };
 
+// Weights of the tiled and cold-segment bf16 kernels: the operand-block copy
+// (gate, up, down regions of E N K elements each) when the problem has one,
+// else the canonical tensors.
+template <bool GATED>
+void tile_weights(const moe_problem& p, const GemmIO& io, const uint16_t*& b0, const uint16_t*& b1) {
+  if (!p.bf16_packed) {
+    b0 = (const uint16_t*)io.B0;
+    b1 = (const uint16_t*)io.B1;
+    return;
+  }
+  const size_t m = (size_t)p.E * (size_t)p.I * (size_t)p.H;
+  const uint16_t* base = (const uint16_t*)p.bf16_packed;
+  b0 = GATED ? base : base + 2 * m;
+  b1 = GATED ? base + m : nullptr;
+}
+
+template <bool GATED, bool PK>
+void launch_big_kernel(int act, dim3 g, dim3 b, hipStream_t s, const moe::big::Params& q) {
+  if constexpr (!GATED) {
+    hipLaunchKernelGGL((moe::big::k_gemm<false, 0, PK>), g, b, 0, s, q);
+  } else {  // one instantiation per activation kind
+    if (act == MOE_ACT_SWIGLU_OAI) hipLaunchKernelGGL((moe::big::k_gemm<true, 1, PK>), g, b, 0, s, q);
+    else if (act == MOE_ACT_SITU) hipLaunchKernelGGL((moe::big::k_gemm<true, 2, PK>), g, b, 0, s, q);
+    else hipLaunchKernelGGL((moe::big::k_gemm<true, 0, PK>), g, b, 0, s, q);
+  }
+}
+
+template <bool GATED, bool PK>
+void launch_cold_kernel(int act, dim3 g, dim3 b, hipStream_t s, const moe::cold::Params& q) {
+  if constexpr (!GATED) {
+    hipLaunchKernelGGL((moe::cold::k_cold<false, 0, PK>), g, b, 0, s, q);
+  } else {
+    if (act == MOE_ACT_SWIGLU_OAI) hipLaunchKernelGGL((moe::cold::k_cold<true, 1, PK>), g, b, 0, s, q);
+    else if (act == MOE_ACT_SITU) hipLaunchKernelGGL((moe::cold::k_cold<true, 2, PK>), g, b, 0, s, q);
+    else hipLaunchKernelGGL((moe::cold::k_cold<true, 0, PK>), g, b, 0, s, q);
+  }
+}
+
 template <bool GATED>
 moe::skinny::Params skinny_params(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws) {
   moe::skinny::Params q;
@@ -539,8 +578,7 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     q.A = (const uint16_t*)io.A;
     q.a_perm = io.a_perm;
     q.a_div = io.a_div;
-    q.B0 = (const uint16_t*)io.B0;
-    q.B1 = (const uint16_t*)io.B1;
+    tile_weights<GATED>(p, io, q.B0, q.B1);
     q.N = io.N;
     q.K = io.K;
     q.tile_seg = tile_seg;
@@ -562,13 +600,8 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     nblk = (nblk + 7) / 8 * 8;
     if (nblk > 0x7fffffffLL) return MOE_ENOTSUP;
     const dim3 g((unsigned)nblk), b(moe::big::NT);
-    if constexpr (!GATED) {
-      hipLaunchKernelGGL((moe::big::k_gemm<false, 0>), g, b, 0, s, q);
-    } else {  // one instantiation per activation kind
-      if (p.act == MOE_ACT_SWIGLU_OAI) hipLaunchKernelGGL((moe::big::k_gemm<true, 1>), g, b, 0, s, q);
-      else if (p.act == MOE_ACT_SITU) hipLaunchKernelGGL((moe::big::k_gemm<true, 2>), g, b, 0, s, q);
-      else hipLaunchKernelGGL((moe::big::k_gemm<true, 0>), g, b, 0, s, q);
-    }
+    if (p.bf16_packed) launch_big_kernel<GATED, true>(p.act, g, b, s, q);
+    else launch_big_kernel<GATED, false>(p.act, g, b, s, q);
   }
   return launch_status();
 }
@@ -580,8 +613,7 @@ int launch_cold(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
   q.A = (const uint16_t*)io.A;
   q.a_perm = io.a_perm;
   q.a_div = io.a_div;
-  q.B0 = (const uint16_t*)io.B0;
-  q.B1 = (const uint16_t*)io.B1;
+  tile_weights<GATED>(p, io, q.B0, q.B1);
   q.N = io.N;
   q.K = io.K;
   q.cold_seg = at<int32_t>(ws, pl.cold_seg);
@@ -599,13 +631,8 @@ int launch_cold(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
   const int rc = device_cus(&q.ncu);
   if (rc) return rc;
   const dim3 g((unsigned)q.ncu), b(moe::cold::NT);
-  if constexpr (!GATED) {
-    hipLaunchKernelGGL((moe::cold::k_cold<false, 0>), g, b, 0, s, q);
-  } else {
-    if (p.act == MOE_ACT_SWIGLU_OAI) hipLaunchKernelGGL((moe::cold::k_cold<true, 1>), g, b, 0, s, q);
-    else if (p.act == MOE_ACT_SITU) hipLaunchKernelGGL((moe::cold::k_cold<true, 2>), g, b, 0, s, q);
-    else hipLaunchKernelGGL((moe::cold::k_cold<true, 0>), g, b, 0, s, q);
-  }
+  if (p.bf16_packed) launch_cold_kernel<GATED, true>(p.act, g, b, s, q);
+  else launch_cold_kernel<GATED, false>(p.act, g, b, s, q);
   return launch_status();
 }
 
@@ -965,6 +992,35 @@ size_t moe_mx_packed_bytes(const moe_problem* p) {
   if (check_problem(p, false)) return 0;
   if (p->wfmt != MOE_W_MXFP4 || p->a_fmt != MOE_A_MXFP8) return 0;
   return (size_t)p->E * (mx_packed_expert1(*p) + mx_packed_expert2(*p));
+}
+
+size_t moe_bf16_packed_bytes(const moe_problem* p) {
+  if (check_problem(p, false)) return 0;
+  if (p->wfmt != MOE_W_BF16) return 0;
+  return (size_t)3 * p->E * (size_t)p->I * (size_t)p->H * 2u;
+}
+
+int moe_bf16_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up, const void* w_down,
+                          void* packed, size_t packed_bytes, moe_stream_t stream) {
+  if (check_problem(p, false)) return MOE_EINVAL;
+  if (p->wfmt != MOE_W_BF16) return MOE_EINVAL;
+  const void* ptrs[] = {w_gate, w_up, w_down, packed};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return MOE_EINVAL;
+  if (packed_bytes < moe_bf16_packed_bytes(p)) return MOE_ENOSPC;
+  const size_t m = (size_t)p->E * (size_t)p->I * (size_t)p->H;  // elements of each matrix set
+  const long long pieces = (long long)(m / 8);                   // H and I are multiples of 64
+  if (pieces == 0) return MOE_OK;
+  const unsigned grid = (unsigned)std::min<long long>((pieces + 255) / 256, 65536);
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* out = (uint16_t*)packed;
+  hipLaunchKernelGGL(moe::big::k_bf16_pack, dim3(grid), dim3(256), 0, s, (const uint16_t*)w_gate, out, p->I, p->H,
+                     pieces);
+  hipLaunchKernelGGL(moe::big::k_bf16_pack, dim3(grid), dim3(256), 0, s, (const uint16_t*)w_up, out + m, p->I, p->H,
+                     pieces);
+  hipLaunchKernelGGL(moe::big::k_bf16_pack, dim3(grid), dim3(256), 0, s, (const uint16_t*)w_down, out + 2 * m, p->H,
+                     p->I, pieces);
+  return launch_status();
 }
 
 int moe_mx_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up, const void* w_down,

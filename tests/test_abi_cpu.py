@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "moe_experts.h")
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -298,3 +298,37 @@ def test_mx_packed_bytes_and_pack_errors():
     r = B.problem(T, H, I, E, 2, "mxfp4", act_fmt="mxfp8")
     r.mx_packed = 1 << 20
     assert B.moe_experts_workspace_bytes(r) > 0
+
+
+def test_bf16_packed_bytes_and_pack_errors():
+    """moe_bf16_packed_bytes: the three weight sets at 2 E I H bytes each (bf16
+    only); moe_bf16_pack_weights and moe_problem.bf16_packed reject what the
+    header says before any launch."""
+    L = B.lib()
+    T, H, I, E = 64, 320, 192, 3
+    p = B.problem(T, H, I, E, 2)
+    assert B.moe_bf16_packed_bytes(p) == 3 * 2 * E * I * H
+    assert B.moe_bf16_packed_bytes(B.problem(T, H, I, E, 2, "mxfp4")) == 0
+    assert B.moe_bf16_packed_bytes(B.problem(T, H, I, 0, 2)) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    need = B.moe_bf16_packed_bytes(p)
+    args = [fake] * 4
+    assert L.moe_bf16_pack_weights(ctypes.byref(p), *args, need - 1, None) == B.MOE_ENOSPC
+    for i in range(4):
+        bad = list(args)
+        bad[i] = None
+        assert L.moe_bf16_pack_weights(ctypes.byref(p), *bad, need, None) == B.MOE_EINVAL
+        bad[i] = ctypes.c_void_p((1 << 20) + 8)
+        assert L.moe_bf16_pack_weights(ctypes.byref(p), *bad, need, None) == B.MOE_EINVAL
+    q = B.problem(T, H, I, E, 2, "mxfp4")
+    assert L.moe_bf16_pack_weights(ctypes.byref(q), *args, need, None) == B.MOE_EINVAL
+    # operand-block weights with MXFP4 weights, or misaligned: the problem is invalid (both entries)
+    for wfmt, ptr in (("mxfp4", 1 << 20), ("bf16", (1 << 20) + 4)):
+        r = B.problem(T, H, I, E, 2, wfmt)
+        r.bf16_packed = ptr
+        assert B.moe_experts_workspace_bytes(r) == 0
+        assert B.moe_experts_grouped_workspace_bytes(r) == 0
+    r = B.problem(T, H, I, E, 2)
+    r.bf16_packed = 1 << 20
+    assert B.moe_experts_workspace_bytes(r) > 0
+    assert B.moe_experts_grouped_workspace_bytes(r) > 0

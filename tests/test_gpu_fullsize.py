@@ -6,7 +6,10 @@ grouped form of moonep_grouped_gemm on the moonep_experts page), so the whole
 output of even the fine-grained layer is checked in well under a minute on
 the host. Before each call the output and the workspace are filled with bf16
 NaN, and both sit between canary bands: a row or tile the kernels never write
-shows up as NaN, and a write outside either buffer changes a band."""
+shows up as NaN, and a write outside either buffer changes a band. bf16
+weights run as the benchmark runs them, in the operand-block layout
+(moe_bf16_pack_weights), after one call on the row layout that must give the
+same bits."""
 import numpy as np
 import pytest
 import torch
@@ -49,18 +52,23 @@ def test_token_major_workload_full_tensor(name):
     p = B.problem(wl.T, wl.H, wl.I, wl.E, wl.k, wl.wfmt, **kw)
     ws = Guarded(B.moe_experts_workspace_bytes(p), DEV)
     out = Guarded(wl.T * wl.H * 2, DEV)
+    packed = B.bf16_pack_weights(p, *W) if wl.wfmt == "bf16" else None
     outs = []
-    for rep in range(2):
+    for rep in range(2 if packed is None else 3):
         ws.poison()
         out.poison()
-        B.experts_forward(x, ids_d, w_d, *W, scales=S, out=out.view_bf16(wl.T, wl.H), workspace=ws.body, **kw)
+        B.experts_forward(x, ids_d, w_d, *W, scales=S, out=out.view_bf16(wl.T, wl.H), workspace=ws.body,
+                          bf16_packed=packed if rep > 0 else None, **kw)
         torch.cuda.synchronize()
         ws.check_bands()
         out.check_bands()
         outs.append(out.view_bf16(wl.T, wl.H).clone())
     assert B.moe_device_error(ws.body) == 0
-    assert torch.equal(outs[0], outs[1]), "run-to-run results differ"
-    got = outs[0].float()
+    assert torch.equal(outs[-2], outs[-1]), "run-to-run results differ"
+    if packed is not None:
+        assert torch.equal(outs[0], outs[1]), "operand-block weights change the result"
+        del packed
+    got = outs[-1].float()
     assert bool(torch.isfinite(got).all()), f"{int((~torch.isfinite(got)).sum())} output values not written"
     mx = wl.wfmt == "mxfp4"
     E = wl.E
@@ -69,7 +77,7 @@ def test_token_major_workload_full_tensor(name):
     else:
         Wo = [LazyExperts(W[i], range(E)) for i in range(3)]
     ref = oracle.experts_forward(to_np(x), ids, w, *Wo, **kw)
-    err = rel_err(to_np(outs[0]), ref)
+    err = rel_err(to_np(outs[-1]), ref)
     counts = np.bincount(ids[(ids >= 0) & (ids < E)].ravel(), minlength=E)
     tiles = row_tiles_covered(counts, 16 if mx or wl.T * wl.k <= 32 * E else 256)
     print(f"[fullsize] {name}: all {wl.T} tokens ({int(counts.sum())} routed rows, {tiles} row tiles), "
@@ -90,22 +98,26 @@ def test_pregrouped_workload_full_tensor():
     p = B.problem(wl.T, wl.H, wl.I, wl.E, 1)
     ws = Guarded(B.moe_experts_grouped_workspace_bytes(p), DEV)
     out = Guarded(wl.T * wl.H * 2, DEV)
+    packed = B.bf16_pack_weights(p, *W)
     outs = []
-    for rep in range(2):
+    for rep in range(3):
         ws.poison()
         out.poison()
-        B.experts_forward_grouped(x, cu_d, rw_d, *W, out=out.view_bf16(wl.T, wl.H), workspace=ws.body)
+        B.experts_forward_grouped(x, cu_d, rw_d, *W, out=out.view_bf16(wl.T, wl.H), workspace=ws.body,
+                                  bf16_packed=packed if rep > 0 else None)
         torch.cuda.synchronize()
         ws.check_bands()
         out.check_bands()
         outs.append(out.view_bf16(wl.T, wl.H).clone())
     assert B.moe_device_error(ws.body) == 0
-    assert torch.equal(outs[0], outs[1])
-    got = outs[0].float()
+    assert torch.equal(outs[1], outs[2])
+    assert torch.equal(outs[0], outs[1]), "operand-block weights change the result"
+    del packed
+    got = outs[-1].float()
     assert bool(torch.isfinite(got).all()), f"{int((~torch.isfinite(got)).sum())} output values not written"
     Wl = [LazyExperts(t, range(wl.E)) for t in W]
     ref = oracle.pregrouped_forward(to_np(x), cu, rw, *Wl)
-    err = rel_err(to_np(outs[0]), ref)
+    err = rel_err(to_np(outs[-1]), ref)
     print(f"[fullsize] pregrouped: all {wl.T} rows over {int(np.sum(lengths > 0))} non-empty segments "
           f"({row_tiles_covered(lengths, 256)} row tiles), max|err|/max|ref| {err:.2e}", flush=True)
     assert err <= TOL

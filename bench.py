@@ -69,8 +69,8 @@ def parse():
     ap.add_argument("--weight-copies", type=int, default=4,
                     help="MXFP4 decode: copies of the weights the steps rotate over")
     ap.add_argument("--row-layout", action="store_true",
-                    help="bf16 workloads: keep the weights in their row layout instead of the operand-block "
-                         "layout made once before the timed steps (moe_bf16_pack_weights)")
+                    help="keep the weights in their canonical layout instead of the kernels' layouts made once "
+                         "before the timed steps (moe_bf16_pack_weights, moe_mx_pack_weights)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -360,18 +360,26 @@ def run_token_major(args, wl, dev, K, act_fmt):
     sets = [(W, S)] + [(tuple(t.clone() for t in W), tuple(t.clone() for t in S) if S[0] is not None else S)
                        for _ in range(copies - 1)]
     p = B.problem(wl.T, wl.H, wl.I, wl.E, wl.k, wl.wfmt, wl.act, wl.alpha, wl.beta, wl.limit, act_fmt=act_fmt)
-    packed = None
-    if B.moe_experts_workspace_layout(p).mx_tiled:
-        # the MXFP4 x MXFP8 prefill kernels' weight format, made once before
-        # the timed steps (flashinfer_moe_ep page, process_weights_after_loading)
-        packed = B.mx_pack_weights(p, *W, *S)
+    packs = None
+    if not args.row_layout:
+        # the kernels' weight layouts, made once per weight copy before the
+        # timed steps (flashinfer_moe_ep page, process_weights_after_loading):
+        # MXFP4 for the prefill GEMMs and the decode kernels' codes, bf16 for
+        # the tiled and cold-segment prefill GEMMs
+        if wl.wfmt == "mxfp4":
+            packs = [B.mx_pack_weights(p, *Wc, *Sc) for Wc, Sc in sets]
+        else:
+            packs = [B.bf16_pack_weights(p, *W)]
         torch.cuda.synchronize()
-        p.mx_packed = packed.data_ptr()
-    elif wl.wfmt == "bf16" and not args.row_layout:
-        # the bf16 prefill kernels' operand-block layout, made the same way
-        packed = B.bf16_pack_weights(p, *W)
-        torch.cuda.synchronize()
-        p.bf16_packed = packed.data_ptr()
+
+    def set_packed(i):
+        if packs is not None:
+            if wl.wfmt == "mxfp4":
+                p.mx_packed = packs[i % len(packs)].data_ptr()
+            else:
+                p.bf16_packed = packs[i % len(packs)].data_ptr()
+
+    set_packed(0)
     ws = B.alloc_workspace(B.moe_experts_workspace_bytes(p), dev)
     out = torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
@@ -384,6 +392,7 @@ def run_token_major(args, wl, dev, K, act_fmt):
 
     def step(i, evs=(), rev=None):
         Wi, Si = sets[i % copies]
+        set_packed(i)
         if args.router:
             if rev is not None:
                 hev.record(rev, stream)
@@ -468,7 +477,7 @@ def run_token_major(args, wl, dev, K, act_fmt):
                    **({"activations": act_fmt} if act_fmt != "bf16" else {}),
                    **({"weight_layout": "packed once before the timed steps ("
                                         + ("moe_mx_pack_weights)" if wl.wfmt == "mxfp4" else "moe_bf16_pack_weights)")}
-                      if packed is not None else {})},
+                      if packs is not None else {})},
         "stage_ms": {s: round(v, 4) for s, v in avg.items()},
         "event_ms_per_step": round(float(np.mean(step_ms)), 4),
         "instrumented_ms_per_step": round(instr_ms, 4),

@@ -137,17 +137,21 @@ typedef struct {
   const float* limit_e;
   const float* fc1_alpha;
   const float* fc2_alpha;
-  /* MXFP4 weights with MXFP8 activations: the weights in the prefill
-   * kernels' own format, written by moe_mx_pack_weights from the same
-   * w_gate / w_up / w_down and scales (device, 16-byte aligned), or NULL (the
-   * zero-initialised default). flashinfer_moe_ep page,
-   * process_weights_after_loading: the weights are put into the kernel's
-   * format once, before the first forward. When set, the token-major prefill
-   * path reads the weights from here and skips the per-call transpose of
-   * their scales; the canonical tensors are still required (the decode
-   * kernels and the pre-grouped entry read them). The library cannot tell a
-   * stale packing from a fresh one: re-pack after changing the weights. Set
-   * with any other weight or activation format: MOE_EINVAL. */
+  /* MXFP4 weights: the weights in the prefill kernels' own format, written
+   * by moe_mx_pack_weights from the same w_gate / w_up / w_down and scales
+   * (device, 16-byte aligned), or NULL (the zero-initialised default).
+   * flashinfer_moe_ep page, process_weights_after_loading: the weights are
+   * put into the kernel's format once, before the first forward. When set,
+   * the token-major MXFP4 x MXFP8 prefill path reads the weights from here
+   * and skips the per-call transpose of their scales, and the
+   * weight-streaming (decode) kernels of both entries read their codes from
+   * here (each 16 rows x 128 K values are then one contiguous 1 KB, already
+   * in MFMA operand order; results bitwise those of the canonical codes).
+   * The canonical tensors are still required (the decode kernels read the
+   * scales from them, and the single-launch decode step reads the codes
+   * too). The library cannot tell a stale packing
+   * from a fresh one: re-pack after changing the weights. Set with bf16
+   * weights: MOE_EINVAL. */
   const void* mx_packed;
   /* bf16 weights: the same weights in the operand-block layout, written by
    * moe_bf16_pack_weights (device, 16-byte aligned), or NULL (the
@@ -219,7 +223,7 @@ typedef struct {
  * the rows' 1 KB e8m0 scale block (row r's four block scales of the stage at
  * r * 4 in the order 0, 2, 1, 3; blocks past K are 0, rows past N repeat row
  * N - 1's). GEMM1's blocks for all experts, then GEMM2's; within an expert
- * column tile major. 0 when p is invalid or not MXFP4 x MXFP8.
+ * column tile major. 0 when p is invalid or its weights are not MXFP4.
  * flashinfer_moe_ep page, process_weights_after_loading. */
 size_t moe_mx_packed_bytes(const moe_problem* p);
 
@@ -227,7 +231,7 @@ size_t moe_mx_packed_bytes(const moe_problem* p);
  * packed (device, 16-byte aligned, caller-owned) from the canonical MXFP4
  * tensors (the moe_experts_forward arguments of the same names), on stream;
  * asynchronous like the forward. Host-side errors before any launch:
- * MOE_EINVAL (invalid p, not MXFP4 x MXFP8, a NULL or misaligned pointer),
+ * MOE_EINVAL (invalid p, weights not MXFP4, a NULL or misaligned pointer),
  * MOE_ENOSPC (packed_bytes below moe_mx_packed_bytes). */
 int moe_mx_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up, const void* w_down,
                         const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down, void* packed,

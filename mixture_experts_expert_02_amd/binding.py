@@ -327,8 +327,9 @@ def experts_forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, scales=None
 
 def experts_forward_grouped(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, scales=None, act="silu", alpha=1.0,
                             beta=0.0, limit=math.inf, out=None, workspace=None, weight_on_input=False,
-                            act_fmt="bf16", expert_params=None, bf16_packed=None) -> torch.Tensor:
-    """Pre-grouped experts step; bf16_packed: the weights packed by bf16_pack_weights (bf16 only), or None."""
+                            act_fmt="bf16", expert_params=None, bf16_packed=None, mx_packed=None) -> torch.Tensor:
+    """Pre-grouped experts step; bf16_packed / mx_packed: the weights packed by bf16_pack_weights /
+    mx_pack_weights (for bf16 / MXFP4 weights), or None."""
     NvS, H = x_nvs.shape
     G = w_gate.shape[0]
     I = w_gate.shape[1]
@@ -336,6 +337,8 @@ def experts_forward_grouped(x_nvs, cu_seqlens, route_w, w_gate, w_up, w_down, sc
     p = problem(NvS, H, I, G, 1, wfmt, act, alpha, beta, limit, weight_on_input, act_fmt, expert_params)
     if bf16_packed is not None:
         p.bf16_packed = bf16_packed.data_ptr()
+    if mx_packed is not None:
+        p.mx_packed = mx_packed.data_ptr()
     if out is None:
         out = torch.empty(NvS, H, dtype=torch.bfloat16, device=x_nvs.device)
     if workspace is None:

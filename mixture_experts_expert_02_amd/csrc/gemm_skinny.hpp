@@ -105,7 +105,21 @@ struct Params {
   const float* row_w;     // route weight per sorted row, or nullptr (weight already on the input)
   ActParams act;
   ExpertParams ep;        // per-expert activation parameters and fc1 / fc2 scales
+  // MXFP4 codes in the packed layout of the MXFP4 prefill GEMMs (PK kernels):
+  // this GEMM's blocks, bp_expert bytes per expert; scales still from S0 / S1
+  const uint8_t* Bp;
+  uint32_t bp_expert;
 };
+
+// The packed MXFP4 layout (written by k_mx_pack, defined with the prefill
+// GEMM): per expert, column tile of PK_COLS1 gate + the same up rows (GEMM1)
+// or PK_COLS2 down rows (GEMM2), and 128-K stage, one PK_BLOCK-byte block whose
+// first bytes hold row r's 64 code bytes at 64 r, 16-byte chunk c at slot
+// c ^ ((r >> 2) & 3); codes past N or K are 0.
+constexpr int PK_BLOCK = 17408;
+constexpr int PK_COLS1 = 128;
+constexpr int PK_COLS2 = 256;
+constexpr int PK_KSTAGE = 128;
 
 __device__ __forceinline__ float sat448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
 
@@ -378,9 +392,13 @@ struct TileLds {
 // or split: hi / lo parts, or MXFP8) with coherent stores and counts its row
 // tile in; GEMM2 starts its weight stream, waits for its row tile, reads the
 // rows with coherent loads, and writes its slot rows coherently.
-template <int FMT, bool GATED, int SPT, bool A8, bool FUSED>
+// PK: MXFP4 codes from the packed layout (p.Bp): a stream's 16 rows of one
+// 128-K step are 1 KB of one block, and lane (l16, q) reads its operand (row
+// l16, chunk q) straight from its swizzled slot, so no register transpose.
+template <int FMT, bool GATED, int SPT, bool A8, bool FUSED, bool PK = false>
 __device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, TileLds<FMT>& L,
                                             const FusedSync& fs) {
+  static_assert(!PK || FMT == W_MXFP4, "packed codes are MXFP4");
   using C = Cfg<FMT>;
   auto& sbuf = L.sbuf;
 
@@ -401,10 +419,12 @@ __device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, Til
   // weight rows of this segment as buffer resources; lane offsets: row, then
   // block q of the first step (MXFP4: 16 bytes per block, bf16: 64)
   const uint32_t rowbytes = FMT == W_MXFP4 ? K / 2 : 2 * K;
-  const uint32_t segbytes = (uint32_t)N * rowbytes;
-  const __amdgpu_buffer_rsrc_t rs0 = weight_rsrc((const uint8_t*)p.B0 + (size_t)seg * segbytes, segbytes);
-  const __amdgpu_buffer_rsrc_t rs1 =
-      weight_rsrc((const uint8_t*)(GATED ? p.B1 : p.B0) + (size_t)seg * segbytes, segbytes);
+  const uint32_t segbytes = PK ? p.bp_expert : (uint32_t)N * rowbytes;  // range of the buffer resources
+  const uint8_t* wb0 = PK ? p.Bp + (size_t)seg * segbytes : (const uint8_t*)p.B0 + (size_t)seg * segbytes;
+  const uint8_t* wb1 = PK ? wb0 : (const uint8_t*)(GATED ? p.B1 : p.B0) + (size_t)seg * segbytes;
+  const __amdgpu_buffer_rsrc_t rs0 = weight_rsrc(wb0, segbytes);
+  const __amdgpu_buffer_rsrc_t rs1 = weight_rsrc(wb1, segbytes);
+  const int KT = (K + PK_KSTAGE - 1) / PK_KSTAGE;  // PK: 128-K stages
   constexpr uint32_t BLOCK_BYTES = FMT == W_MXFP4 ? 16 : 64;
   // bf16: lane (l16, q) loads its own blocks. MXFP4: a chunk is 256 bytes of
   // each of a stream's 16 rows, loaded as 4 rows x 256 bytes per instruction,
@@ -415,7 +435,17 @@ __device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, Til
   // of step u.
   uint32_t vo0[FMT == W_MXFP4 ? 4 : 1], vo1[FMT == W_MXFP4 ? 4 : 1];
   const int piece = 4 * (l16 >> 2) + q;  // MXFP4: this lane's 16-byte block of a chunk's 256 bytes
-  if (FMT == W_MXFP4) {
+  if (PK) {  // vo[u]: step u of chunk 0 = stage u of the column tile's blocks
+    constexpr int CT = GATED ? PK_COLS1 : PK_COLS2;
+    const int ct = nb / CT, r0 = nb % CT + l16, r1 = (GATED ? PK_COLS1 : 16) + r0;
+    const uint32_t lo0 = 64u * r0 + 16u * (q ^ ((r0 >> 2) & 3));
+    const uint32_t lo1 = 64u * r1 + 16u * (q ^ ((r1 >> 2) & 3));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      vo0[u] = (uint32_t)(ct * KT + u) * PK_BLOCK + lo0;
+      vo1[u] = (uint32_t)(ct * KT + u) * PK_BLOCK + lo1;
+    }
+  } else if (FMT == W_MXFP4) {
     const int b1 = GATED ? nb : nb + 16;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -532,6 +562,16 @@ __device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, Til
   // are not read either (their offset is moved past the segment too); the
   // next row's bytes would only meet zero activations.
   auto load_chunk = [&](WSet<FMT>& w, int c) {
+    if constexpr (PK) {  // stages past the last (K tail, chunks past the last) read 0 without an access
+      const int so = c < nch ? c * C::SPC * PK_BLOCK : 0;
+#pragma unroll
+      for (int u = 0; u < C::SPC; ++u) {
+        const bool in_k = c < nch && c * C::SPC + u < KT;
+        w.w0[u].q[0] = __builtin_amdgcn_raw_buffer_load_b128(rs0, in_k ? vo0[u] : segbytes, so, 0);
+        w.w1[u].q[0] = __builtin_amdgcn_raw_buffer_load_b128(rs1, in_k ? vo1[u] : segbytes, so, 0);
+      }
+      return;
+    }
     const int so = c < nch ? c * C::SPC * 4 * BLOCK_BYTES : (int)segbytes;
     const bool in_row = (uint32_t)so + 16u * (FMT == W_MXFP4 ? piece : l16) < rowbytes;
 #pragma unroll
@@ -558,8 +598,10 @@ __device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, Til
       // per step (see quad_transpose)
       u32x4 t0[4] = {w.w0[0].q[0], w.w0[1].q[0], w.w0[2].q[0], w.w0[3].q[0]};
       u32x4 t1[4] = {w.w1[0].q[0], w.w1[1].q[0], w.w1[2].q[0], w.w1[3].q[0]};
-      quad_transpose(t0, lane);
-      quad_transpose(t1, lane);
+      if constexpr (!PK) {  // packed codes arrive in the operand layout
+        quad_transpose(t0, lane);
+        quad_transpose(t1, lane);
+      }
       const uint8_t* hrow = &sbuf[buf][l16 * C::QROW];
       const uint8_t* lrow = hrow + BM * C::QROW;
       const uint8_t* srow = &sbuf[buf][2 * BM * C::QROW + 16 * l16];
@@ -746,11 +788,11 @@ __device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, Til
 }
 
 // One tile per workgroup: blockIdx.x = row tile x column tiles + column tile.
-template <int FMT, bool GATED, int SPT, bool A8 = false>
+template <int FMT, bool GATED, int SPT, bool A8 = false, bool PK = false>
 __global__ __launch_bounds__(NT) void k_gemm(const Params p) {
   __shared__ TileLds<FMT> L;
   const int mt = blockIdx.x / p.n_tiles;
-  skinny_tile<FMT, GATED, SPT, A8, false>(p, mt, blockIdx.x - mt * p.n_tiles, L, FusedSync{});
+  skinny_tile<FMT, GATED, SPT, A8, false, PK>(p, mt, blockIdx.x - mt * p.n_tiles, L, FusedSync{});
 }
 
 // The combine of the single launch: token t's slot rows, j ascending in fp32

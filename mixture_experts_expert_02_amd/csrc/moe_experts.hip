@@ -138,8 +138,7 @@ int check_problem(const moe_problem* p, bool grouped) {
   if (p->weight_on_input != 0 && p->weight_on_input != 1) return MOE_EINVAL;
   if (p->a_fmt != MOE_A_BF16 && p->a_fmt != MOE_A_MXFP8) return MOE_EINVAL;
   if (p->a_fmt == MOE_A_MXFP8 && p->wfmt != MOE_W_MXFP4) return MOE_ENOTSUP;  // block-scaled MFMA path only
-  if (p->mx_packed && (p->wfmt != MOE_W_MXFP4 || p->a_fmt != MOE_A_MXFP8 || !aligned16(p->mx_packed)))
-    return MOE_EINVAL;
+  if (p->mx_packed && (p->wfmt != MOE_W_MXFP4 || !aligned16(p->mx_packed))) return MOE_EINVAL;
   if (p->bf16_packed && (p->wfmt != MOE_W_BF16 || !aligned16(p->bf16_packed))) return MOE_EINVAL;
   const void* ep[] = {p->alpha_e, p->beta_e, p->limit_e, p->fc1_alpha, p->fc2_alpha};
   for (const void* q : ep)
@@ -442,6 +441,18 @@ int set_attrs() {
       (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 4, true>,
       (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 8, true>,
       (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 16, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, true, 4, false, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, true, 8, false, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, true, 16, false, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 4, false, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 8, false, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 16, false, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, true, 4, true, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, true, 8, true, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, true, 16, true, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 4, true, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 8, true, true>,
+      (const void*)moe::skinny::k_gemm<moe::skinny::W_MXFP4, false, 16, true, true>,
   };
   for (const void* f : mx)
     if (e == hipSuccess)
@@ -540,7 +551,30 @@ moe::skinny::Params skinny_params(const moe_problem& p, const Plan& pl, const Ge
   q.row_w = io.row_w;
   q.act = act_params(p);
   q.ep = expert_params(p);
+  // packed MXFP4 codes (read by the PK kernels of the separate launches)
+  q.Bp = nullptr;
+  q.bp_expert = 0;
+  if (p.mx_packed && p.wfmt == MOE_W_MXFP4) {
+    q.Bp = (const uint8_t*)p.mx_packed + (GATED ? 0 : (size_t)p.E * mx_packed_expert1(p));
+    q.bp_expert = (uint32_t)(GATED ? mx_packed_expert1(p) : mx_packed_expert2(p));
+  }
   return q;
+}
+
+static_assert(moe::skinny::PK_BLOCK == moe::mx::PK_STAGE && moe::skinny::PK_KSTAGE == moe::mx::BK &&
+                  moe::skinny::PK_COLS1 == moe::mx::BN / 2 && moe::skinny::PK_COLS2 == moe::mx::BN,
+              "the decode kernels read the MXFP4 prefill GEMMs' packed layout");
+
+// MXFP4 decode GEMM: SPT scale pieces per thread, A8 MXFP8 activations, PK packed codes
+template <bool GATED, bool A8, bool PK>
+void launch_skinny_mx(int spt, dim3 grid, dim3 block, size_t lds, hipStream_t s, const moe::skinny::Params& q) {
+  using moe::skinny::k_gemm;
+  using moe::skinny::W_MXFP4;
+  switch (spt) {
+    case 4: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 4, A8, PK>), grid, block, lds, s, q); break;
+    case 8: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 8, A8, PK>), grid, block, lds, s, q); break;
+    default: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 16, A8, PK>), grid, block, lds, s, q); break;
+  }
 }
 
 template <bool GATED>
@@ -556,20 +590,14 @@ int launch_gemm(const moe_problem& p, const Plan& pl, const GemmIO& io, void* ws
     using moe::skinny::k_gemm;
     using moe::skinny::W_BF16;
     using moe::skinny::W_MXFP4;
-    if (p.wfmt == MOE_W_MXFP4 && p.a_fmt == MOE_A_MXFP8) {
+    if (p.wfmt == MOE_W_MXFP4) {
       const size_t lds = moe::skinny::scale_lds_bytes(io.K);
-      switch (moe::skinny::scale_pieces_per_thread(io.K)) {
-        case 4: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 4, true>), grid, block, lds, s, q); break;
-        case 8: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 8, true>), grid, block, lds, s, q); break;
-        default: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 16, true>), grid, block, lds, s, q); break;
-      }
-    } else if (p.wfmt == MOE_W_MXFP4) {
-      const size_t lds = moe::skinny::scale_lds_bytes(io.K);
-      switch (moe::skinny::scale_pieces_per_thread(io.K)) {
-        case 4: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 4>), grid, block, lds, s, q); break;
-        case 8: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 8>), grid, block, lds, s, q); break;
-        default: hipLaunchKernelGGL((k_gemm<W_MXFP4, GATED, 16>), grid, block, lds, s, q); break;
-      }
+      const int spt = moe::skinny::scale_pieces_per_thread(io.K);
+      const bool a8 = p.a_fmt == MOE_A_MXFP8;
+      if (a8 && q.Bp) launch_skinny_mx<GATED, true, true>(spt, grid, block, lds, s, q);
+      else if (a8) launch_skinny_mx<GATED, true, false>(spt, grid, block, lds, s, q);
+      else if (q.Bp) launch_skinny_mx<GATED, false, true>(spt, grid, block, lds, s, q);
+      else launch_skinny_mx<GATED, false, false>(spt, grid, block, lds, s, q);
     } else {
       hipLaunchKernelGGL((k_gemm<W_BF16, GATED, 0>), grid, block, 0, s, q);
     }
@@ -990,7 +1018,7 @@ extern "C" {
 
 size_t moe_mx_packed_bytes(const moe_problem* p) {
   if (check_problem(p, false)) return 0;
-  if (p->wfmt != MOE_W_MXFP4 || p->a_fmt != MOE_A_MXFP8) return 0;
+  if (p->wfmt != MOE_W_MXFP4) return 0;
   return (size_t)p->E * (mx_packed_expert1(*p) + mx_packed_expert2(*p));
 }
 
@@ -1027,7 +1055,7 @@ int moe_mx_pack_weights(const moe_problem* p, const void* w_gate, const void* w_
                         const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down, void* packed,
                         size_t packed_bytes, moe_stream_t stream) {
   if (check_problem(p, false)) return MOE_EINVAL;
-  if (p->wfmt != MOE_W_MXFP4 || p->a_fmt != MOE_A_MXFP8) return MOE_EINVAL;
+  if (p->wfmt != MOE_W_MXFP4) return MOE_EINVAL;
   const void* ptrs[] = {w_gate, w_up, w_down, s_gate, s_up, s_down, packed};
   for (const void* q : ptrs)
     if (!q || !aligned16(q)) return MOE_EINVAL;

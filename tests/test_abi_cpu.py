@@ -269,14 +269,15 @@ def test_misaligned_expert_param_pointer_rejected():
 
 def test_mx_packed_bytes_and_pack_errors():
     """moe_mx_packed_bytes: one 17408-byte block per expert, column tile and
-    128-K stage of each GEMM (MXFP4 x MXFP8 only); moe_mx_pack_weights and
+    128-K stage of each GEMM (MXFP4 weights, either activation format: the
+    decode kernels read the codes too); moe_mx_pack_weights and
     moe_problem.mx_packed reject what the header says before any launch."""
     L = B.lib()
     T, H, I, E = 64, 2880, 2880, 4
     p = B.problem(T, H, I, E, 2, "mxfp4", "swiglu_oai", 1.702, 1.0, 7.0, act_fmt="mxfp8")
     blocks = E * (math.ceil(I / 128) * math.ceil(H / 128) + math.ceil(H / 256) * math.ceil(I / 128))
     assert B.moe_mx_packed_bytes(p) == blocks * 17408
-    assert B.moe_mx_packed_bytes(B.problem(T, H, I, E, 2, "mxfp4", act_fmt="bf16")) == 0
+    assert B.moe_mx_packed_bytes(B.problem(T, H, I, E, 2, "mxfp4", act_fmt="bf16")) == blocks * 17408
     assert B.moe_mx_packed_bytes(B.problem(T, H, I, E, 2)) == 0
     fake = ctypes.c_void_p(1 << 20)
     need = B.moe_mx_packed_bytes(p)
@@ -288,16 +289,19 @@ def test_mx_packed_bytes_and_pack_errors():
         assert L.moe_mx_pack_weights(ctypes.byref(p), *bad, need, None) == B.MOE_EINVAL
         bad[i] = ctypes.c_void_p((1 << 20) + 8)
         assert L.moe_mx_pack_weights(ctypes.byref(p), *bad, need, None) == B.MOE_EINVAL
-    q = B.problem(T, H, I, E, 2, "mxfp4", act_fmt="bf16")
+    q = B.problem(T, H, I, E, 2)
     assert L.moe_mx_pack_weights(ctypes.byref(q), *args, need, None) == B.MOE_EINVAL
-    # packed weights with another format, or misaligned: the problem is invalid
-    for wfmt, afmt, ptr in (("bf16", "bf16", 1 << 20), ("mxfp4", "bf16", 1 << 20), ("mxfp4", "mxfp8", (1 << 20) + 4)):
+    # packed weights with bf16 weights, or misaligned: the problem is invalid
+    for wfmt, afmt, ptr in (("bf16", "bf16", 1 << 20), ("mxfp4", "bf16", (1 << 20) + 4),
+                            ("mxfp4", "mxfp8", (1 << 20) + 4)):
         r = B.problem(T, H, I, E, 2, wfmt, act_fmt=afmt)
         r.mx_packed = ptr
         assert B.moe_experts_workspace_bytes(r) == 0
-    r = B.problem(T, H, I, E, 2, "mxfp4", act_fmt="mxfp8")
-    r.mx_packed = 1 << 20
-    assert B.moe_experts_workspace_bytes(r) > 0
+        assert B.moe_experts_grouped_workspace_bytes(r) == 0
+    for afmt in ("bf16", "mxfp8"):
+        r = B.problem(T, H, I, E, 2, "mxfp4", act_fmt=afmt)
+        r.mx_packed = 1 << 20
+        assert B.moe_experts_workspace_bytes(r) > 0
 
 
 def test_bf16_packed_bytes_and_pack_errors():

@@ -6,10 +6,10 @@ grouped form of moonep_grouped_gemm on the moonep_experts page), so the whole
 output of even the fine-grained layer is checked in well under a minute on
 the host. Before each call the output and the workspace are filled with bf16
 NaN, and both sit between canary bands: a row or tile the kernels never write
-shows up as NaN, and a write outside either buffer changes a band. bf16
-weights run as the benchmark runs them, in the operand-block layout
-(moe_bf16_pack_weights), after one call on the row layout that must give the
-same bits."""
+shows up as NaN, and a write outside either buffer changes a band. The
+weights run as the benchmark runs them, in the kernels' layouts
+(moe_bf16_pack_weights, moe_mx_pack_weights), after one call on the
+canonical layout that must give the same bits."""
 import numpy as np
 import pytest
 import torch
@@ -52,22 +52,22 @@ def test_token_major_workload_full_tensor(name):
     p = B.problem(wl.T, wl.H, wl.I, wl.E, wl.k, wl.wfmt, **kw)
     ws = Guarded(B.moe_experts_workspace_bytes(p), DEV)
     out = Guarded(wl.T * wl.H * 2, DEV)
-    packed = B.bf16_pack_weights(p, *W) if wl.wfmt == "bf16" else None
+    packed = B.bf16_pack_weights(p, *W) if wl.wfmt == "bf16" else B.mx_pack_weights(p, *W, *S)
+    pk = "bf16_packed" if wl.wfmt == "bf16" else "mx_packed"
     outs = []
-    for rep in range(2 if packed is None else 3):
+    for rep in range(3):
         ws.poison()
         out.poison()
         B.experts_forward(x, ids_d, w_d, *W, scales=S, out=out.view_bf16(wl.T, wl.H), workspace=ws.body,
-                          bf16_packed=packed if rep > 0 else None, **kw)
+                          **{pk: packed if rep > 0 else None}, **kw)
         torch.cuda.synchronize()
         ws.check_bands()
         out.check_bands()
         outs.append(out.view_bf16(wl.T, wl.H).clone())
     assert B.moe_device_error(ws.body) == 0
     assert torch.equal(outs[-2], outs[-1]), "run-to-run results differ"
-    if packed is not None:
-        assert torch.equal(outs[0], outs[1]), "operand-block weights change the result"
-        del packed
+    assert torch.equal(outs[0], outs[1]), "the packed weights change the result"
+    del packed
     got = outs[-1].float()
     assert bool(torch.isfinite(got).all()), f"{int((~torch.isfinite(got)).sum())} output values not written"
     mx = wl.wfmt == "mxfp4"

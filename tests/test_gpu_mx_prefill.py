@@ -253,3 +253,56 @@ def test_mx_prefill_packed_weights_bitwise(name, shape, act, extra):
     b = B.experts_forward(xd, idd, wd, *Wd, scales=Sd, mx_packed=packed, **act_kw)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ decode kernels on packed codes
+DECODE_PK_CASES = [
+    # name, (T, H, I, E, k), act, activation format
+    ("silu", (13, 192, 128, 5, 2), "silu", "bf16"),
+    ("swiglu_col_tail", (9, 256, 320, 6, 3), "swiglu_oai", "bf16"),  # I = 320: half a column tile, 2.5 K stages
+    ("ktail", (6, 2880, 192, 4, 2), "swiglu_oai", "bf16"),           # H = 2880: 22.5 K stages in GEMM1
+    ("many_rows", (150, 128, 256, 3, 2), "silu", "bf16"),            # several 16-row tiles per expert
+    ("mxfp8", (9, 256, 320, 6, 3), "swiglu_oai", "mxfp8"),
+    ("mxfp8_ktail", (6, 2880, 192, 4, 2), "situ", "mxfp8"),
+]
+
+
+@pytest.mark.parametrize("name,shape,act,afmt", DECODE_PK_CASES, ids=[c[0] for c in DECODE_PK_CASES])
+def test_decode_packed_codes_bitwise(name, shape, act, afmt):
+    """The weight-streaming kernels reading their codes from the packed layout
+    (moe_problem.mx_packed) give outputs bit for bit equal to the canonical
+    codes': the same codes meet the same activations in the same order, and
+    K past the end meets zero activations either way."""
+    T, H, I, E, k = shape
+    print(f"[mx_packed] decode {name} T={T} H={H} I={I} E={E} k={k} {act} {afmt}", flush=True)
+    x, ids, w, W, S = make_problem(21, T, H, I, E, k, "mxfp4")
+    kw = dict(act=act, **ACT_PARAMS[act])
+    p = B.problem(T, H, I, E, k, "mxfp4", act_fmt=afmt, **kw)
+    assert not B.moe_experts_workspace_layout(p).mx_tiled
+    Wd, Sd = [t.to(DEV) for t in W], [t.to(DEV) for t in S]
+    packed = B.mx_pack_weights(p, *Wd, *Sd)
+    xd, idd, wd = x.to(DEV), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
+    a = B.experts_forward(xd, idd, wd, *Wd, scales=Sd, act_fmt=afmt, **kw)
+    b = B.experts_forward(xd, idd, wd, *Wd, scales=Sd, act_fmt=afmt, mx_packed=packed, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_decode_packed_codes_grouped_bitwise():
+    """Pre-grouped entry with MXFP4 weights (weight-streaming kernels): packed
+    codes against canonical ones, segments of 0, 2, 17 and 40 rows, K = 320."""
+    H, I = 320, 256
+    lengths = np.array([2, 0, 17, 40], dtype=np.int64)
+    G, NvS = len(lengths), int(lengths.sum())
+    print(f"[mx_packed] grouped decode NvS={NvS} H={H} I={I} G={G}", flush=True)
+    x, _, _, W, S = make_problem(23, NvS, H, I, G, 1, "mxfp4")
+    rw = np.random.default_rng(4).random(NvS).astype(np.float32)
+    cu = np.cumsum(lengths).astype(np.int32)
+    p = B.problem(NvS, H, I, G, 1, "mxfp4")
+    Wd, Sd = [t.to(DEV) for t in W], [t.to(DEV) for t in S]
+    packed = B.mx_pack_weights(p, *Wd, *Sd)
+    args = (x.to(DEV), torch.from_numpy(cu).to(DEV), torch.from_numpy(rw).to(DEV), *Wd)
+    a = B.experts_forward_grouped(*args, scales=Sd)
+    b = B.experts_forward_grouped(*args, scales=Sd, mx_packed=packed)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -1,7 +1,9 @@
 """moe_experts_forward_noalloc (the library's own scratch as workspace)
 against moe_experts_forward on the same inputs: calls in a row, the second
 on a smaller problem than the first, each bitwise equal to the workspace
-entry point's output and within the tolerance of the oracle."""
+entry point's output and within the tolerance of the oracle; the calls on
+MXFP4 and bf16 weights also run on the packed weight layouts, with the
+same bits."""
 import numpy as np
 import pytest
 import torch
@@ -45,6 +47,13 @@ def test_noalloc_matches_workspace_entry_two_calls():
     want = oracle.experts_forward(to_np(x), ids, w, *[(c.cpu().numpy(), s.cpu().numpy()) for c, s in
                                                      ((cg, sg), (cu, su), (cd, sd))], **kw)
     assert rel_err(to_np(got), want) <= TOL
+    # the same call on the packed codes (moe_problem.mx_packed)
+    packed = B.mx_pack_weights(p, cg, cu, cd, sg, su, sd)
+    p.mx_packed = packed.data_ptr()
+    ref_p, got_p = both(p, x, ids_d, w_d, (cg, cu, cd), (sg, su, sd))
+    assert torch.equal(ref_p, ref) and torch.equal(got_p, ref)
+    p.mx_packed = None
+    del packed
     # call 2: a smaller MXFP4 problem (fewer tokens, smaller sizes) on the same scratch
     T, H, I, E, k = 9, 256, 320, 6, 3
     print(f"[noalloc] call 2: mxfp4 T={T} H={H} I={I} E={E} k={k}", flush=True)
@@ -66,6 +75,12 @@ def test_noalloc_matches_workspace_entry_two_calls():
     assert torch.equal(ref3, got3)
     want3 = oracle.experts_forward(to_np(x3), ids3, w3, *[to_np(t) for t in W3])
     assert rel_err(to_np(got3), want3) <= TOL
+    # the same call on the operand-block weights (moe_problem.bf16_packed)
+    W3d = [t.to(DEV) for t in W3]
+    packed3 = B.bf16_pack_weights(p3, *W3d)
+    p3.bf16_packed = packed3.data_ptr()
+    ref3p, got3p = both(p3, x3.to(DEV), torch.from_numpy(ids3).to(DEV), torch.from_numpy(w3).to(DEV), W3d, None)
+    assert torch.equal(ref3p, ref3) and torch.equal(got3p, ref3)
 
 
 def test_noalloc_rejects_problems_beyond_the_scratch():

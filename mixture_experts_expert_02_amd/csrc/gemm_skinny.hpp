@@ -230,10 +230,11 @@ struct WSet {
   WChunk<FMT> w0[Cfg<FMT>::SPC], w1[Cfg<FMT>::SPC];
 };
 
-// Weight loads go through a buffer resource over one segment's weight rows:
-// a lane's block offset needs no clamping, since a block past a row's end
-// reads the next row (finite codes that meet zero activations) or, past the
-// segment's last row, reads 0; the per-step offsets become immediates.
+// Weight loads go through a buffer resource over one segment's weight rows.
+// Every load whose bytes lie past its row's end, or past the last chunk, gets
+// a VGPR offset past the segment and reads 0 without a memory access; the
+// SGPR offset, which carries a chunk's K position, is not relied on for the
+// range check.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -572,8 +573,11 @@ __device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, Til
       }
       return;
     }
-    const int so = c < nch ? c * C::SPC * 4 * BLOCK_BYTES : (int)segbytes;
-    const bool in_row = (uint32_t)so + 16u * (FMT == W_MXFP4 ? piece : l16) < rowbytes;
+    // chunks past the last: the VGPR offset itself lies past the segment
+    // (the range check covers the VGPR offset, not the SGPR one)
+    const bool live = c < nch;
+    const int so = live ? c * C::SPC * 4 * BLOCK_BYTES : 0;
+    const bool in_row = live && (uint32_t)so + 16u * (FMT == W_MXFP4 ? piece : l16) < rowbytes;
 #pragma unroll
     for (int u = 0; u < C::SPC; ++u) {
       if (FMT == W_MXFP4) {  // w.w0[u]: instruction u (rows 4 u + l16 % 4)
@@ -581,10 +585,11 @@ __device__ __forceinline__ void skinny_tile(const Params& p, int mt, int nt, Til
         w.w1[u].q[0] = __builtin_amdgcn_raw_buffer_load_b128(rs1, in_row ? vo1[u] : segbytes, so, 0);
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) {  // 16 bytes past the row end read 0 (w_operand_bf16 zeroes them anyway)
           const uint32_t o = 4 * BLOCK_BYTES * u + 16 * i;
-          w.w0[u].q[i] = __builtin_amdgcn_raw_buffer_load_b128(rs0, vo0[0] + o, so, 0);
-          w.w1[u].q[i] = __builtin_amdgcn_raw_buffer_load_b128(rs1, vo1[0] + o, so, 0);
+          const bool inr = live && (uint32_t)so + BLOCK_BYTES * q + o < rowbytes;
+          w.w0[u].q[i] = __builtin_amdgcn_raw_buffer_load_b128(rs0, inr ? vo0[0] + o : segbytes, so, 0);
+          w.w1[u].q[i] = __builtin_amdgcn_raw_buffer_load_b128(rs1, inr ? vo1[0] + o : segbytes, so, 0);
         }
       }
     }

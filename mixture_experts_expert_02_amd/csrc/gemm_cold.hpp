@@ -117,11 +117,13 @@ __global__ __launch_bounds__(NT, 8) void k_cold(const Params p) {
     __syncthreads();  // the last item's reads of the staging buffers are done
     u32x4 ar = *(const u32x4*)ap;
     *(u32x4*)&sa[0][sl] = ar;
+    // weights are read once: non-temporal loads (nt), so that the stream
+    // leaves the cached panels of the tiled kernel beside it in place
     u32x4 wb[2][2];  // weights of two steps: [step & 1][stream]
-    wb[0][0] = *(const u32x4*)b0;
-    wb[0][1] = *(const u32x4*)b1;
-    wb[1][0] = *(const u32x4*)(b0 + SSTEP);
-    wb[1][1] = *(const u32x4*)(b1 + SSTEP);
+    wb[0][0] = __builtin_nontemporal_load((const u32x4*)b0);
+    wb[0][1] = __builtin_nontemporal_load((const u32x4*)b1);
+    wb[1][0] = __builtin_nontemporal_load((const u32x4*)(b0 + SSTEP));
+    wb[1][1] = __builtin_nontemporal_load((const u32x4*)(b1 + SSTEP));
     __syncthreads();
 
     f32x4 acc[2][2];
@@ -147,8 +149,8 @@ __global__ __launch_bounds__(NT, 8) void k_cold(const Params p) {
           acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bv1, acc[1][1], 0, 0, 0);
         }
         if (s + 2 < 2 * nch) {
-          wb[j][0] = *(const u32x4*)(b0 + (s + 2) * SSTEP);
-          wb[j][1] = *(const u32x4*)(b1 + (s + 2) * SSTEP);
+          wb[j][0] = __builtin_nontemporal_load((const u32x4*)(b0 + (s + 2) * SSTEP));
+          wb[j][1] = __builtin_nontemporal_load((const u32x4*)(b1 + (s + 2) * SSTEP));
         }
       }
       if (more) *(u32x4*)&sa[(c + 1) & 1][sl] = ar;

@@ -26,7 +26,7 @@ struct SplitSum {
 // consecutive columns, slot j outer and K range s inner, both ascending. The
 // (j, s) rows are fetched eight at a time before any is added, so a thread
 // has up to eight loads in flight instead of one; the additions keep the
-// order above.
+// order above. Each slot row is read once: non-temporal loads.
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* y, const int32_t* inv_perm, int T, int k,
                                                  int H, const SplitSum ss, uint16_t* out) {
   const int t = blockIdx.x;
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* y, const int32_
         const int j = idx / S, sp = idx - j * S;
         const int p = idx < n ? ip[j] : -1;
         ok[u] = p >= 0;
-        if (ok[u]) v[u] = *(const u32x4*)(y + (size_t)sp * ss.stride + (size_t)p * H + h);
+        if (ok[u]) v[u] = __builtin_nontemporal_load((const u32x4*)(y + (size_t)sp * ss.stride + (size_t)p * H + h));
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {

@@ -223,8 +223,8 @@ typedef struct {
  * the rows' 1 KB e8m0 scale block (row r's four block scales of the stage at
  * r * 4 in the order 0, 2, 1, 3; blocks past K are 0, rows past N repeat row
  * N - 1's). GEMM1's blocks for all experts, then GEMM2's; within an expert
- * column tile major. 0 when p is invalid or its weights are not MXFP4.
- * flashinfer_moe_ep page, process_weights_after_loading. */
+ * column tile major. 0 when p is invalid or its weights are not MXFP4 (k is
+ * not looked at). flashinfer_moe_ep page, process_weights_after_loading. */
 size_t moe_mx_packed_bytes(const moe_problem* p);
 
 /* Writes the packed weights of problem p (moe_mx_packed_bytes bytes) into
@@ -244,7 +244,8 @@ int moe_mx_pack_weights(const moe_problem* p, const void* w_gate, const void* w_
  * kb) * 1024 bytes from its region's start, its 16-byte piece l (l < 64)
  * holding row 16 nb + l % 16, values 32 kb + 8 (l / 16)..+7 (the B operand of
  * v_mfma_f32_16x16x32_bf16, lane by lane). 0 when p is invalid or its weights
- * are not bf16. flashinfer_moe_ep page, process_weights_after_loading. */
+ * are not bf16 (k is not looked at: the layout serves both entries).
+ * flashinfer_moe_ep page, process_weights_after_loading. */
 size_t moe_bf16_packed_bytes(const moe_problem* p);
 
 /* Writes the operand-block weights of problem p (moe_bf16_packed_bytes bytes)

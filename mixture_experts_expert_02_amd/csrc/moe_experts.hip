@@ -1017,20 +1017,20 @@ int forward_impl(const moe_problem* p, const void* x, const int32_t* ids, const 
 extern "C" {
 
 size_t moe_mx_packed_bytes(const moe_problem* p) {
-  if (check_problem(p, false)) return 0;
+  if (check_problem(p, true)) return 0;
   if (p->wfmt != MOE_W_MXFP4) return 0;
   return (size_t)p->E * (mx_packed_expert1(*p) + mx_packed_expert2(*p));
 }
 
 size_t moe_bf16_packed_bytes(const moe_problem* p) {
-  if (check_problem(p, false)) return 0;
+  if (check_problem(p, true)) return 0;
   if (p->wfmt != MOE_W_BF16) return 0;
   return (size_t)3 * p->E * (size_t)p->I * (size_t)p->H * 2u;
 }
 
 int moe_bf16_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up, const void* w_down,
                           void* packed, size_t packed_bytes, moe_stream_t stream) {
-  if (check_problem(p, false)) return MOE_EINVAL;
+  if (check_problem(p, true)) return MOE_EINVAL;
   if (p->wfmt != MOE_W_BF16) return MOE_EINVAL;
   const void* ptrs[] = {w_gate, w_up, w_down, packed};
   for (const void* q : ptrs)
@@ -1054,7 +1054,7 @@ int moe_bf16_pack_weights(const moe_problem* p, const void* w_gate, const void* 
 int moe_mx_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up, const void* w_down,
                         const uint8_t* s_gate, const uint8_t* s_up, const uint8_t* s_down, void* packed,
                         size_t packed_bytes, moe_stream_t stream) {
-  if (check_problem(p, false)) return MOE_EINVAL;
+  if (check_problem(p, true)) return MOE_EINVAL;
   if (p->wfmt != MOE_W_MXFP4) return MOE_EINVAL;
   const void* ptrs[] = {w_gate, w_up, w_down, s_gate, s_up, s_down, packed};
   for (const void* q : ptrs)

@@ -314,6 +314,7 @@ def test_bf16_packed_bytes_and_pack_errors():
     assert B.moe_bf16_packed_bytes(p) == 3 * 2 * E * I * H
     assert B.moe_bf16_packed_bytes(B.problem(T, H, I, E, 2, "mxfp4")) == 0
     assert B.moe_bf16_packed_bytes(B.problem(T, H, I, 0, 2)) == 0
+    assert B.moe_bf16_packed_bytes(B.problem(T, H, I, E, 0)) == 3 * 2 * E * I * H  # k is not looked at
     fake = ctypes.c_void_p(1 << 20)
     need = B.moe_bf16_packed_bytes(p)
     args = [fake] * 4
